@@ -1,0 +1,523 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``pin_*`` returns True when the oracle agrees with something it does not
+compute itself: a closed form, a library routine (torch's scaled-dot-product
+attention and logsumexp on the CPU, scipy's logsumexp and softmax), a brute force
+that uses a different algorithm, or the structural facts the pages print.  The
+pin tests assert them; the mutation tests plant mistakes in the oracle and assert
+that at least one pin notices.
+"""
+
+import json
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ tree structure
+
+def _children(parent_row, n):
+    kids = [[] for _ in range(n)]
+    for i in range(1, n):
+        kids[int(parent_row[i])].append(i)
+    return kids
+
+
+def brute_ancestry(parent_row, n):
+    """(depth, ancestor matrix) by breadth-first search from the root and by
+    collecting each node's subtree -- no upward walks."""
+    kids = _children(parent_row, n)
+    depth = [-1] * n
+    depth[0] = 0
+    queue = [0]
+    while queue:
+        j = queue.pop(0)
+        for c in kids[j]:
+            depth[c] = depth[j] + 1
+            queue.append(c)
+    is_anc = np.zeros((n, n), dtype=bool)          # is_anc[i, j]: j is i or an ancestor of i
+    for j in range(n):
+        stack = [j]
+        while stack:
+            x = stack.pop()
+            is_anc[x, j] = True
+            stack.extend(kids[x])
+    return np.asarray(depth), is_anc
+
+
+def pin_tree_example():
+    """The pages' depth-3, 10-token example tree (reading of its lost figure)."""
+    fx = json.load(open(os.path.join(GOLDEN, "eagle1_example_tree.json")))
+    facts = fx["facts_printed_by_the_page"]
+    par = np.asarray(fx["reading_parent"], dtype=np.int32)
+    n = len(par)
+    anc, depth, pos, st = oracle.tree_build(par[None, :], [n], [0])
+    ok = st[0] == 0 and n == facts["example_tree_tokens"]
+    ok &= int(depth[0].max()) == facts["example_tree_depth"]
+    ok &= n > int(depth[0].max())
+    # left-heavy: at every level, children counts never increase from left to right
+    kids = _children(par, n)
+    for d in range(int(depth[0].max()) + 1):
+        level = [i for i in range(n) if depth[0, i] == d]
+        counts = [len(kids[i]) for i in level]
+        ok &= counts == sorted(counts, reverse=True)
+    # the bitsets written out by hand from the parent array: node -> {itself, ancestors}
+    by_hand = [0x1, 0x3, 0x5, 0x9, 0x1 | 0x2 | 0x10, 0x1 | 0x2 | 0x20, 0x1 | 0x4 | 0x40,
+               0x1 | 0x2 | 0x10 | 0x80, 0x1 | 0x2 | 0x10 | 0x100, 0x1 | 0x2 | 0x20 | 0x200]
+    ok &= [int(a) for a in anc[0, :n]] == by_hand
+    ok &= list(depth[0, :n]) == [0, 1, 1, 1, 2, 2, 2, 3, 3, 3]
+    return bool(ok)
+
+
+def pin_tree_closed_forms(n=64):
+    chain = synth.random_parents(None, n, "chain")
+    star = synth.random_parents(None, n, "star")
+    par = np.stack([chain, star])
+    anc, depth, pos, st = oracle.tree_build(par, [n, n], [7, 0])
+    ok = list(st) == [0, 0]
+    ok &= all(int(anc[0, i]) == (1 << (i + 1)) - 1 for i in range(n))
+    ok &= all(int(depth[0, i]) == i and int(pos[0, i]) == 7 + i for i in range(n))
+    ok &= all(int(anc[1, i]) == (1 | (1 << i)) for i in range(n))
+    ok &= all(int(depth[1, i]) == (0 if i == 0 else 1) for i in range(n))
+    return bool(ok)
+
+
+def pin_tree_bruteforce(seed, trials=20):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(rng.integers(1, 65))
+        shape = ["random", "chain", "star", "broom"][t % 4]
+        par = synth.random_parents(rng, n, shape)
+        row = np.full(64, -1, dtype=np.int32)
+        row[:n] = par
+        L = int(rng.integers(0, 5000))
+        anc, depth, pos, st = oracle.tree_build(row[None, :], [n], [L])
+        bd, bm = brute_ancestry(par, n)
+        if st[0] != 0 or not np.array_equal(depth[0, :n], bd) or not np.array_equal(pos[0, :n], bd + L):
+            return False
+        for i in range(n):
+            bits = int(anc[0, i])
+            if [bool((bits >> j) & 1) for j in range(n)] != list(bm[i]) or bits >> n:
+                return False
+        if np.any(anc[0, n:] != 0) or np.any(depth[0, n:] != -1):
+            return False
+    return True
+
+
+def pin_tree_status():
+    S = oracle
+    cases = [  # (parent prefix, n, expected status)
+        ([-1, 0, 1], 3, S.STATUS_OK),
+        ([0, 0, 1], 3, S.STATUS_BAD_PARENT),          # root with a parent
+        ([-1, 0, 2], 3, S.STATUS_BAD_PARENT),         # parent == self
+        ([-1, 2, 0], 3, S.STATUS_BAD_PARENT),         # parent after the child
+        ([-1, -5, 0], 3, S.STATUS_BAD_PARENT),        # parent below -1
+        ([-1, 0, -1], 3, S.STATUS_SECOND_ROOT),
+        ([-1, -1, 7], 3, S.STATUS_SECOND_ROOT),       # the first offending node decides
+        ([-1, 0, 1], 0, S.STATUS_BAD_N),
+        ([-1, 0, 1], 65, S.STATUS_BAD_N),
+    ]
+    for par, n, want in cases:
+        row = np.full(64, -1, dtype=np.int32)
+        row[:len(par)] = par
+        anc, depth, pos, st = oracle.tree_build(row[None, :], [n], None)
+        if st[0] != want:
+            return False
+        if want != 0 and (np.any(anc != 0) or np.any(depth != -1) or np.any(pos != -1)):
+            return False
+    return True
+
+
+# ------------------------------------------------------------------ attention
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+
+
+def _case(seed, B=3, Hq=4, Hkv=2, D=16, lens=(9, 0, 3), n=(12, 6, 1), shapes=None):
+    inp, parent, nn = synth.random_attention_case(seed, B, Hq, Hkv, D, lens, n, dtype="f32",
+                                                  std=1.0, n_max=64, shapes=shapes)
+    return inp, parent, nn
+
+
+def _oracle_attn(inp, parent, nn):
+    return oracle.tree_verify_attn(inp.q, inp.k_tree, inp.v_tree, inp.k_prefix, inp.v_prefix,
+                                   inp.prefix_offsets, parent, nn)
+
+
+def pin_attn_path_invariant(seed=1, tol=1e-10):
+    """Each node's output = plain attention of that one query over prefix ++ its
+    root path (library SDPA, no mask), and lse = torch.logsumexp of the scores."""
+    inp, parent, nn = _case(seed)
+    out, lse = _oracle_attn(inp, parent, nn)
+    B, _, Hq, D = inp.q.shape
+    G = Hq // inp.k_tree.shape[2]
+    for b in range(B):
+        o0, o1 = inp.prefix_offsets[b], inp.prefix_offsets[b + 1]
+        _, is_anc = brute_ancestry(parent[b], int(nn[b]))
+        for i in range(int(nn[b])):
+            path = [j for j in range(int(nn[b])) if is_anc[i, j]]
+            for h in range(Hq):
+                g = h // G
+                keys = np.concatenate([inp.k_prefix[o0:o1, g], inp.k_tree[b, path, g]])
+                vals = np.concatenate([inp.v_prefix[o0:o1, g], inp.v_tree[b, path, g]])
+                qq = _t(inp.q[b, i, h])[None, None, :]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq, _t(keys)[None], _t(vals)[None], scale=1.0 / np.sqrt(D))[0, 0].numpy()
+                l_ref = torch.logsumexp(_t(keys) @ _t(inp.q[b, i, h]) / np.sqrt(D), 0).item()
+                if np.max(np.abs(ref - out[b, i, h])) > tol or abs(l_ref - lse[b, i, h]) > tol:
+                    return False
+    return True
+
+
+def pin_attn_chain_is_causal(seed=2, L=11, n=13, tol=1e-10):
+    """A chain tree equals causal attention over prefix ++ chain (library SDPA, is_causal)."""
+    inp, parent, nn = _case(seed, B=1, Hq=2, Hkv=1, D=16, lens=(L,), n=(n,), shapes=["chain"])
+    out, _ = _oracle_attn(inp, parent, nn)
+    D = inp.q.shape[3]
+    for h in range(2):
+        keys = np.concatenate([inp.k_prefix[:, 0], inp.k_tree[0, :n, 0]])
+        vals = np.concatenate([inp.v_prefix[:, 0], inp.v_tree[0, :n, 0]])
+        qs = np.concatenate([np.zeros((L, D), np.float32), inp.q[0, :n, h]])   # prefix rows unused
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            _t(qs)[None], _t(keys)[None], _t(vals)[None], is_causal=True,
+            scale=1.0 / np.sqrt(D))[0, L:].numpy()
+        if np.max(np.abs(ref - out[0, :n, h])) > tol:
+            return False
+    return True
+
+
+def pin_attn_star(seed=3, L=5, n=9, tol=1e-10):
+    """In a star every node sees the prefix, the root and itself -- nothing else."""
+    inp, parent, nn = _case(seed, B=1, Hq=1, Hkv=1, D=16, lens=(L,), n=(n,), shapes=["star"])
+    out, _ = _oracle_attn(inp, parent, nn)
+    D = inp.q.shape[3]
+    for i in range(n):
+        sel = [0] if i == 0 else [0, i]
+        keys = np.concatenate([inp.k_prefix[:, 0], inp.k_tree[0, sel, 0]])
+        vals = np.concatenate([inp.v_prefix[:, 0], inp.v_tree[0, sel, 0]])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            _t(inp.q[0, i, 0])[None, None], _t(keys)[None], _t(vals)[None],
+            scale=1.0 / np.sqrt(D))[0, 0].numpy()
+        if np.max(np.abs(ref - out[0, i, 0])) > tol:
+            return False
+    return True
+
+
+def pin_attn_empty_prefix(seed=4, n=10, tol=1e-10):
+    """L = 0: pure tree attention, the root sees only itself (its output is its own V)."""
+    inp, parent, nn = _case(seed, B=1, Hq=2, Hkv=2, D=16, lens=(0,), n=(n,))
+    out, lse = _oracle_attn(inp, parent, nn)
+    D = inp.q.shape[3]
+    ok = np.max(np.abs(out[0, 0, :] - inp.v_tree[0, 0, :].astype(np.float64))) <= tol
+    for h in range(2):
+        l_root = float(inp.q[0, 0, h].astype(np.float64) @ inp.k_tree[0, 0, h].astype(np.float64)) / np.sqrt(D)
+        ok &= abs(lse[0, 0, h] - l_root) <= tol
+    return bool(ok)
+
+
+def pin_attn_one_hot_mask(seed=5, n=40, L=7, D=128):
+    """Exact mask probe: tree V rows are unit vectors e_j and prefix V is zero in the
+    first 64 coordinates, so out[i][j] is exactly 0 off i's path and > 0 on it."""
+    inp, parent, nn = _case(seed, B=1, Hq=2, Hkv=1, D=D, lens=(L,), n=(n,))
+    inp.v_tree[:] = 0
+    for j in range(n):
+        inp.v_tree[0, j, 0, j] = 1.0
+    inp.v_prefix[:, :, :64] = 0
+    out, _ = _oracle_attn(inp, parent, nn)
+    _, is_anc = brute_ancestry(parent[0], n)
+    for i in range(n):
+        for h in range(2):
+            on = out[0, i, h, :n] > 0
+            off = out[0, i, h, :n] == 0.0
+            if not (np.array_equal(on, is_anc[i]) and np.array_equal(off, ~is_anc[i])):
+                return False
+    return True
+
+
+def pin_attn_sibling_relabel(seed=6, tol=1e-12):
+    """Relabelling siblings (keeping parent < child) permutes the outputs the same way."""
+    inp, parent, nn = _case(seed, B=1, Hq=2, Hkv=1, D=16, lens=(4,), n=(6,))
+    par = np.array([-1, 0, 0, 0, 1, 2] + [-1] * 58, dtype=np.int32)[None]
+    out, _ = _oracle_attn(inp, par, nn)
+    perm = [0, 2, 1, 3, 5, 4]           # new index of each old node: swap 1<->2 and 4<->5
+    par2 = np.full_like(par, -1)
+    for old in range(6):
+        par2[0, perm[old]] = -1 if old == 0 else perm[par[0, old]]
+    inp2 = synth.AttnInputs(**{**inp.__dict__})
+    for name in ("q", "k_tree", "v_tree"):
+        a = getattr(inp, name).copy()
+        a[0, perm] = getattr(inp, name)[0, :6]
+        setattr(inp2, name, a)
+    out2, _ = _oracle_attn(inp2, par2, nn)
+    return bool(np.max(np.abs(out2[0, perm] - out[0, :6])) <= tol)
+
+
+def pin_attn_one_matches_full(seed=7):
+    inp, parent, nn = _case(seed)
+    out, lse = _oracle_attn(inp, parent, nn)
+    for b in range(3):
+        for i in range(int(nn[b])):
+            for h in range(4):
+                o, l = oracle.attention.tree_verify_attn_one(
+                    inp.q, inp.k_tree, inp.v_tree, inp.k_prefix, inp.v_prefix, inp.prefix_offsets,
+                    parent, b, h, i)
+                if np.max(np.abs(o - out[b, i, h])) > 1e-12 or abs(l - lse[b, i, h]) > 1e-12:
+                    return False
+    return True
+
+
+# ------------------------------------------------------------------ expansion / rerank
+
+def quantised_logits(rng, shape):
+    """Logits on a 0.5 grid so that equal logits and equal scores are common."""
+    return (rng.integers(-8, 9, size=shape) * 0.5).astype(np.float32)
+
+
+def brute_expand_one(levels, k, m, root):
+    """One sequence, nodes named by their token path; every ranking is a plain sorted()."""
+    V = levels[0].shape[-1]
+    everything = []                    # (path, score, creation)
+    frontier = [((), np.float32(0.0))]
+    made = 0
+    for rows in levels:
+        cand = []
+        for f, (path, sc) in enumerate(frontier):
+            row = rows[f]
+            lse32 = np.float32(scipy.special.logsumexp(row.astype(np.float64)))
+            for t in sorted(range(V), key=lambda t: (-float(row[t]), t))[:k]:
+                cand.append((path + (t,), np.float32(sc + np.float32(row[t] - lse32)), made))
+                made += 1
+        everything += cand
+        frontier = [(p, s) for p, s, _ in sorted(cand, key=lambda x: (-float(x[1]), x[2]))[:k]]
+    kept = sorted(everything, key=lambda x: (-float(x[1]), x[2]))[:m - 1]
+    kept.sort(key=lambda x: (len(x[0]), x[2]))
+    paths = [()] + [p for p, _, _ in kept]
+    parent = [-1] + [paths.index(p[:-1]) for p, _, _ in kept]
+    token = [root] + [p[-1] for p, _, _ in kept]
+    score = [np.float32(0.0)] + [s for _, s, _ in kept]
+    return parent, token, score
+
+
+def _levels(rng, B, S, k, V, quant=True):
+    out = []
+    for s in range(S):
+        shape = (B, 1 if s == 0 else k, V)
+        out.append(quantised_logits(rng, shape) if quant else
+                   (rng.standard_normal(shape) * 2).astype(np.float32))
+    return out
+
+
+def pin_expand_bruteforce(seed=11, trials=12):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        k = [1, 2, 3][t % 3]
+        S = 1 + t % 3
+        V = 16
+        B = 2
+        levels = _levels(rng, B, S, k, V, quant=(t % 2 == 0))
+        m = int(rng.integers(1, 12))
+        roots = rng.integers(0, V, size=B)
+        res = oracle.expand_rerank(levels, k, m, roots, n_max=64)
+        for b in range(B):
+            par, tok, sc = brute_expand_one([lv[b] for lv in levels], k, m, int(roots[b]))
+            n = len(par)
+            if res.status[b] != 0 or res.n_nodes[b] != n:
+                return False
+            if list(res.parent[b, :n]) != par or list(res.token[b, :n]) != tok:
+                return False
+            if res.score[b, :n].tobytes() != np.asarray(sc, np.float32).tobytes():
+                return False
+    return True
+
+
+def pin_expand_closed_forms(seed=12):
+    rng = np.random.default_rng(seed)
+    ok = True
+    # k = 1: a chain of the row argmaxes (lowest id among equal maxima)
+    levels = _levels(rng, 1, 5, 1, 16)
+    res = oracle.expand_rerank(levels, 1, 64, [3])
+    ok &= res.n_nodes[0] == 6 and list(res.parent[0, :6]) == [-1, 0, 1, 2, 3, 4]
+    ok &= list(res.token[0, 1:6]) == [int(np.flatnonzero(lv[0, 0] == lv[0, 0].max())[0]) for lv in levels]
+    # one level: a star of the m-1 best root-row tokens in logit order
+    levels = _levels(rng, 1, 1, 6, 16)
+    res = oracle.expand_rerank(levels, 6, 5, [0])
+    row = levels[0][0, 0]
+    best = sorted(range(16), key=lambda t: (-float(row[t]), t))[:4]
+    ok &= res.n_nodes[0] == 5 and list(res.parent[0, :5]) == [-1, 0, 0, 0, 0]
+    ok &= list(res.token[0, 1:5]) == best
+    # m - 1 >= pool keeps every generated node: k + (S-1) k^2
+    levels = _levels(rng, 1, 3, 2, 16)
+    res = oracle.expand_rerank(levels, 2, 64, [0])
+    ok &= res.n_nodes[0] == 1 + 2 + 2 * 4
+    return bool(ok)
+
+
+def pin_expand_value_is_path_product(seed=13, tol=2e-5):
+    """exp(score) equals the product of the softmax confidences along the node's path
+    (the global-acceptance value), computed with scipy's softmax in float64.  Two
+    levels, so every level-1 token is distinct and names its logit row uniquely."""
+    rng = np.random.default_rng(seed)
+    k, V = 4, 50
+    levels = _levels(rng, 1, 2, k, V, quant=False)
+    res = oracle.expand_rerank(levels, k, 64, [0])
+    n = int(res.n_nodes[0])
+    if n != 1 + k + k * k:
+        return False
+    par, tok = res.parent[0], res.token[0]
+    rank_of = {int(t): r for r, t in enumerate(res.frontier_tokens[0][0])}
+    for i in range(1, n):
+        if par[i] == 0:
+            prob = scipy.special.softmax(levels[0][0, 0].astype(np.float64))[tok[i]]
+        else:
+            p = par[i]
+            prob = (scipy.special.softmax(levels[0][0, 0].astype(np.float64))[tok[p]] *
+                    scipy.special.softmax(levels[1][0, rank_of[int(tok[p])]].astype(np.float64))[tok[i]])
+        if abs(np.exp(np.float64(res.score[0, i])) - prob) > tol * prob:
+            return False
+    return True
+
+
+def pin_expand_invariants(seed=14):
+    """Ancestor closure, scores never increase along a path, kept = the best m-1 by
+    (score, creation) -- on 2*N(0,1) logits as in the dynamic-tree workloads."""
+    rng = np.random.default_rng(seed)
+    levels = _levels(rng, 3, 5, 4, 200, quant=False)
+    res = oracle.expand_rerank(levels, 4, [20, 64, 2], [1, 2, 3])
+    ok = list(res.status) == [0, 0, 0]
+    ok &= list(res.n_nodes) == [20, 64, 2]          # pool = 4 + 4 * 16 = 68 >= 63
+    for b in range(3):
+        n = int(res.n_nodes[b])
+        for i in range(1, n):
+            p = res.parent[b, i]
+            ok &= 0 <= p < i and res.score[b, i] <= res.score[b, p]
+    return bool(ok)
+
+
+def pin_expand_nonfinite():
+    rng = np.random.default_rng(15)
+    levels = _levels(rng, 2, 2, 2, 16, quant=False)
+    levels[1][1, 1, 5] = np.nan
+    res = oracle.expand_rerank(levels, 2, 5, [0, 0])
+    return bool(res.status[0] == 0 and res.status[1] == oracle.STATUS_NONFINITE
+                and res.n_nodes[1] == 0 and np.all(res.parent[1] == -1))
+
+
+# ------------------------------------------------------------------ acceptance
+
+def brute_accept_one(par, tok, tgt, n):
+    """Top-down: from the root, step into every child whose token equals the target's
+    token after the current node; keep the deepest node reached (lowest index on ties)."""
+    kids = _children(par, n)
+    best, best_d = 0, 0
+    stack = [(0, 0)]
+    while stack:
+        x, d = stack.pop()
+        if d > best_d or (d == best_d and x < best):
+            best, best_d = x, d
+        for c in kids[x]:
+            if int(tok[c]) == int(tgt[x]):
+                stack.append((c, d + 1))
+    path = []
+    j = best
+    while j != 0:
+        path.append(j)
+        j = int(par[j])
+    return best_d, best, int(tgt[best]), path[::-1]
+
+
+def pin_accept_bruteforce(seed=21, trials=200):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(rng.integers(1, 65))
+        par = np.full(64, -1, dtype=np.int32)
+        par[:n] = synth.random_parents(rng, n, ["random", "chain", "star", "broom"][t % 4])
+        V = [2, 3, 5, 32000][t % 4]              # small vocabularies make duplicates common
+        tok = rng.integers(0, V, size=64).astype(np.int32)
+        tgt = rng.integers(0, V, size=64).astype(np.int32)
+        al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [n])
+        d, bb, bo, pp = brute_accept_one(par, tok, tgt, n)
+        if (al[0], best[0], bonus[0]) != (d, bb, bo) or list(path[0, :d]) != pp or np.any(path[0, d:] != -1):
+            return False
+    return True
+
+
+def pin_accept_closed_forms():
+    n = 9
+    chain = np.full(64, -1, np.int32)
+    chain[:n] = synth.random_parents(None, n, "chain")
+    tok = np.arange(100, 164, dtype=np.int32)
+    tgt_all = np.roll(tok, -1).astype(np.int32)      # target after node i is node i+1's token
+    al, best, bonus, path = oracle.tree_accept(chain[None], tok[None], tgt_all[None], [n])
+    ok = al[0] == n - 1 and best[0] == n - 1 and bonus[0] == tgt_all[n - 1]
+    ok &= list(path[0, :n - 1]) == list(range(1, n))
+    tgt_none = np.full(64, 7, np.int32)
+    al, best, bonus, path = oracle.tree_accept(chain[None], tok[None], tgt_none[None], [n])
+    ok &= al[0] == 0 and best[0] == 0 and bonus[0] == 7 and np.all(path[0] == -1)
+    # duplicate siblings: nodes 1 and 2 both carry the target's token; 2 leads deeper
+    par = np.full(64, -1, np.int32)
+    par[:5] = [-1, 0, 0, 2, 1]
+    tok = np.zeros(64, np.int32)
+    tok[:5] = [0, 5, 5, 6, 9]
+    tgt = np.zeros(64, np.int32)
+    tgt[:5] = [5, 8, 6, 4, 3]
+    al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [5])
+    ok &= al[0] == 2 and best[0] == 3 and bonus[0] == 4 and list(path[0, :2]) == [2, 3]
+    # equal depth: lowest index wins
+    tgt[:5] = [5, 9, 6, 4, 3]
+    al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [5])
+    ok &= al[0] == 2 and best[0] == 3
+    tok[4] = 9
+    tgt[2] = 1
+    al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [5])
+    ok &= al[0] == 2 and best[0] == 4 and list(path[0, :2]) == [1, 4]
+    # root only
+    al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [1])
+    ok &= al[0] == 0 and best[0] == 0 and bonus[0] == tgt[0]
+    # invalid trees give -1
+    al, best, bonus, path = oracle.tree_accept(par[None], tok[None], tgt[None], [0])
+    ok &= al[0] == -1 and best[0] == -1 and bonus[0] == -1
+    return bool(ok)
+
+
+ALL_PINS = {
+    "tree_example": pin_tree_example,
+    "tree_closed_forms": pin_tree_closed_forms,
+    "tree_bruteforce": lambda: pin_tree_bruteforce(0),
+    "tree_status": pin_tree_status,
+    "attn_path_invariant": pin_attn_path_invariant,
+    "attn_chain_is_causal": pin_attn_chain_is_causal,
+    "attn_star": pin_attn_star,
+    "attn_empty_prefix": pin_attn_empty_prefix,
+    "attn_one_hot_mask": pin_attn_one_hot_mask,
+    "attn_sibling_relabel": pin_attn_sibling_relabel,
+    "attn_one_matches_full": pin_attn_one_matches_full,
+    "expand_bruteforce": pin_expand_bruteforce,
+    "expand_closed_forms": pin_expand_closed_forms,
+    "expand_value_is_path_product": pin_expand_value_is_path_product,
+    "expand_invariants": pin_expand_invariants,
+    "expand_nonfinite": pin_expand_nonfinite,
+    "accept_bruteforce": pin_accept_bruteforce,
+    "accept_closed_forms": pin_accept_closed_forms,
+}
+
+
+def failing_pins(names=None):
+    """Names of pins that fail (or raise) -- used by the mutation tests."""
+    bad = []
+    for name, fn in ALL_PINS.items():
+        if names is not None and name not in names:
+            continue
+        try:
+            if not fn():
+                bad.append(name)
+        except Exception:
+            bad.append(name)
+    return bad

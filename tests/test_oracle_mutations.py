@@ -1,0 +1,96 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin notices.
+
+Each mutation replaces one helper of the oracle through monkeypatch; the pins in
+``oracle_pins`` must then fail.  This is what makes the pins worth trusting: a
+dropped term, a wrong index, a transposed operand or a flipped tie-break anywhere
+in the oracle is caught by at least one of them.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.accept
+import oracle.attention
+import oracle.expand
+import oracle.tree
+import oracle_pins
+
+
+_ORIG_WALK = oracle.tree.path_to_root
+
+
+def _walk_without_self(parent_row, i):
+    return _ORIG_WALK(parent_row, i)[1:]
+
+
+def _walk_without_root(parent_row, i):
+    w = _ORIG_WALK(parent_row, i)
+    return w[:-1] if len(w) > 1 else w
+
+
+def _walk_off_by_one(parent_row, i):
+    w = _ORIG_WALK(parent_row, i)
+    return [j + 1 if j + 1 < len(parent_row) and j != 0 else j for j in w]
+
+
+def _mask_with_siblings(parent_row, n, L):
+    mask = np.zeros((n, L + n), dtype=bool)
+    mask[:, :L] = True
+    for i in range(n):
+        for j in _ORIG_WALK(parent_row, i):
+            mask[i, L + j] = True
+            for s in range(1, n):
+                if parent_row[s] == parent_row[j] and j != 0:
+                    mask[i, L + s] = True
+    return mask
+
+
+def _attend_transposed(qrows, keys, values, mask_rows, scale):
+    return _ORIG_ATTEND(qrows, values, keys, mask_rows, scale)
+
+
+def _attend_no_scale(qrows, keys, values, mask_rows, scale):
+    return _ORIG_ATTEND(qrows, keys, values, mask_rows, 1.0)
+
+
+def _attend_lse_without_max(qrows, keys, values, mask_rows, scale):
+    out, lse = _ORIG_ATTEND(qrows, keys, values, mask_rows, scale)
+    s = np.where(mask_rows, (qrows @ keys.T) * scale, -np.inf)
+    return out, lse - s.max(axis=1)
+
+
+_ORIG_ATTEND = oracle.attention._attend
+
+MUTATIONS = {
+    "tree: walk drops the node itself": [(oracle.tree, "path_to_root", _walk_without_self)],
+    "tree: walk index off by one": [(oracle.tree, "path_to_root", _walk_off_by_one)],
+    "attention: root missing from the path": [(oracle.attention, "path_to_root", _walk_without_root)],
+    "attention: self missing from the path": [(oracle.attention, "path_to_root", _walk_without_self)],
+    "attention: siblings leak into the mask": [(oracle.attention, "tree_mask", _mask_with_siblings)],
+    "attention: K and V transposed": [(oracle.attention, "_attend", _attend_transposed)],
+    "attention: 1/sqrt(D) scale dropped": [(oracle.attention, "_attend", _attend_no_scale)],
+    "attention: lse without the max term": [(oracle.attention, "_attend", _attend_lse_without_max)],
+    "expand: top-k ties to the higher id": [
+        (oracle.expand, "row_topk", lambda row, k: (len(row) - 1 - np.argsort(-row[::-1], kind="stable"))[:k])],
+    "expand: ranking ties to the later node": [
+        (oracle.expand, "rank_key", lambda score, creation: (-float(score), -int(creation)))],
+    "expand: scores not normalised": [
+        (oracle.expand, "row_log_normaliser", lambda row: (np.float32(0.0), 0.0))],
+    "expand: ascending score order": [
+        (oracle.expand, "rank_key", lambda score, creation: (float(score), int(creation)))],
+    "accept: compares with the node's own target": [
+        (oracle.accept, "node_passes", lambda par, tok, tgt, j: int(tok[j]) == int(tgt[j]))],
+    "accept: walk drops the node itself": [(oracle.accept, "path_to_root", _walk_without_self)],
+}
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    for module, attr, repl in MUTATIONS[name]:
+        monkeypatch.setattr(module, attr, repl)
+    assert oracle_pins.failing_pins(), f"no pin noticed: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert oracle_pins.failing_pins() == []
