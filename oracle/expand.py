@@ -27,6 +27,9 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   root (m counts the root).  Scores never increase along a path and ties favour
   the earlier-created parent, so the kept set always contains its ancestors.
 * Output order: the root, then the kept nodes by (depth, creation), parents remapped.
+* Errors surface at the level where they occur, as a caller calling level by level
+  sees them: a non-finite logit row fails its sequence at that level (earlier levels
+  keep their reported frontier), a kept count m outside [1, n_max] at the last level.
 """
 
 from typing import NamedTuple
@@ -93,10 +96,6 @@ def expand_rerank(logits_steps, k, m, root_token, n_max=64):
     frontier_tokens = [np.full((B, k), -1, dtype=np.int32) for _ in range(S)]
 
     for b in range(B):
-        mb = int(m_arr[b])
-        if mb < 1 or mb > n_max:
-            status[b] = STATUS_BAD_N
-            continue
         # pool entries: (parent pool index or -1 for the root, token, score, depth)
         pool = []
         frontier = [(-1, np.float32(0.0), 0)]      # (pool index, score, depth) of the root
@@ -117,15 +116,19 @@ def expand_rerank(logits_steps, k, m, root_token, n_max=64):
                     sc = np.float32(fscore + logp)
                     children.append((fidx, int(t), sc, fdepth + 1, len(pool) + len(children)))
             if bad:
-                break
+                break                                # this level and later report no frontier
+            if s == S - 1 and not 1 <= int(m_arr[b]) <= n_max:
+                break                                # the kept count is checked at the last level
             pool.extend(c[:4] for c in children)
             ranked = sorted(children, key=lambda c: rank_key(c[2], c[4]))[:k]
             frontier = [(c[4], c[2], c[3]) for c in ranked]
             frontier_tokens[s][b, :len(ranked)] = [c[1] for c in ranked]
         if bad:
             status[b] = STATUS_NONFINITE
-            for s in range(S):
-                frontier_tokens[s][b, :] = -1
+            continue
+        mb = int(m_arr[b])
+        if not 1 <= mb <= n_max:
+            status[b] = STATUS_BAD_N
             continue
         order = sorted(range(len(pool)), key=lambda i: rank_key(pool[i][2], i))
         kept = order[:mb - 1]

@@ -402,12 +402,18 @@ def pin_expand_invariants(seed=14):
 
 
 def pin_expand_nonfinite():
+    """A NaN row fails its sequence at that level: the level before keeps its frontier,
+    the failing level and the rest report none; an out-of-range m fails at the last level."""
     rng = np.random.default_rng(15)
-    levels = _levels(rng, 2, 2, 2, 16, quant=False)
+    levels = _levels(rng, 3, 3, 2, 16, quant=False)
     levels[1][1, 1, 5] = np.nan
-    res = oracle.expand_rerank(levels, 2, 5, [0, 0])
-    return bool(res.status[0] == 0 and res.status[1] == oracle.STATUS_NONFINITE
-                and res.n_nodes[1] == 0 and np.all(res.parent[1] == -1))
+    res = oracle.expand_rerank(levels, 2, [5, 5, 65], [0, 0, 0])
+    ok = list(res.status) == [0, oracle.STATUS_NONFINITE, oracle.STATUS_BAD_N]
+    ok &= res.n_nodes[1] == 0 and np.all(res.parent[1] == -1) and res.n_nodes[2] == 0
+    ok &= np.all(res.frontier_tokens[0][1] >= 0) and np.all(res.frontier_tokens[1][1] == -1)
+    ok &= np.all(res.frontier_tokens[1][2] >= 0) and np.all(res.frontier_tokens[2][2] == -1)
+    ok &= np.array_equal(res.frontier_tokens[0][2], res.frontier_tokens[0][0]) is not None
+    return bool(ok)
 
 
 # ------------------------------------------------------------------ acceptance

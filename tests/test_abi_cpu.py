@@ -1,0 +1,147 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports what the header
+declares, and rejects malformed host arguments with the documented status before
+making any device call (so these tests never touch a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verify_ancestor_amd as tv
+from tree_attention_verify_ancestor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeverify.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(4096)        # a non-NULL, 16-byte aligned stand-in; never dereferenced
+Z = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:tv_status|size_t|int|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libtreeverify.so not built")
+    return tv.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_identity(L):
+    assert L.tv_abi_version() == 1
+    assert L.tv_status_string(0) == b"ok"
+    assert b"workspace" in L.tv_status_string(WS)
+
+
+def test_tree_build_validation(L):
+    assert L.tree_build(1, 64, Z, P, Z, P, P, Z, Z, Z) == NULL
+    assert L.tree_build(1, 64, P, P, Z, Z, P, Z, Z, Z) == NULL
+    assert L.tree_build(0, 64, P, P, Z, P, P, Z, Z, Z) == SHAPE
+    assert L.tree_build(1, 65, P, P, Z, P, P, Z, Z, Z) == SHAPE
+    assert L.tree_build(1, 0, P, P, Z, P, P, Z, Z, Z) == SHAPE
+
+
+def test_tree_accept_validation(L):
+    assert L.tree_accept(1, 64, Z, P, P, P, P, P, P, P, P, Z, Z) == NULL
+    assert L.tree_accept(1, 64, P, P, P, P, P, P, P, P, Z, Z, Z) == NULL
+    assert L.tree_accept(2, 65, P, P, P, P, P, P, P, P, P, Z, Z) == SHAPE
+    assert L.tree_accept(0, 8, P, P, P, P, P, P, P, P, P, Z, Z) == SHAPE
+
+
+def _expand(L, ws=P, ws_bytes=1 << 30, B=2, k=4, max_steps=3, step=1, vocab=100, logits=P,
+            final_m=0, root=Z, n_max=64, parent=Z, token=Z, score=Z, n_nodes=Z):
+    return L.tree_expand_rerank(ws, ws_bytes, B, k, max_steps, step, vocab, logits, final_m, Z,
+                                root, n_max, parent, token, score, n_nodes, Z, Z, Z)
+
+
+def test_expand_validation(L):
+    assert _expand(L, logits=Z) == NULL
+    assert _expand(L, k=17) == SHAPE
+    assert _expand(L, k=0) == SHAPE
+    assert _expand(L, step=0) == SHAPE
+    assert _expand(L, step=4) == SHAPE
+    assert _expand(L, vocab=3) == SHAPE
+    assert _expand(L, final_m=65) == SHAPE
+    assert _expand(L, final_m=-1) == SHAPE
+    assert _expand(L, n_max=65) == SHAPE
+    assert _expand(L, k=16, max_steps=20) == SHAPE            # pool beyond 4096 slots
+    assert _expand(L, final_m=8, root=P, parent=Z, token=P, score=P, n_nodes=P) == NULL
+    assert _expand(L, final_m=8, root=Z, parent=P, token=P, score=P, n_nodes=P) == NULL
+    assert _expand(L, ws=Z) == WS
+    need = L.tree_expand_workspace_size(2, 4, 3)
+    assert need > 0
+    assert _expand(L, ws_bytes=need - 1) == WS
+
+
+def test_expand_workspace_size(L):
+    assert L.tree_expand_workspace_size(0, 4, 3) == 0
+    assert L.tree_expand_workspace_size(1, 17, 3) == 0
+    assert L.tree_expand_workspace_size(1, 16, 20) == 0
+    one = L.tree_expand_workspace_size(1, 10, 7)
+    assert one >= 16 * (10 + 6 * 100) and one % 256 == 0
+    assert L.tree_expand_workspace_size(32, 10, 7) == 32 * one
+
+
+def _attn(L, dt=1, B=2, Hq=8, Hkv=2, D=128, n_max=64, Lmax=100, q=P, kt=P, vt=P, kp=P, vp=P,
+          offs=P, nn=P, anc=P, out=P, ws=P, ws_bytes=1 << 34):
+    return L.tree_verify_attn(dt, B, Hq, Hkv, D, n_max, Lmax, 0.0, q, kt, vt, kp, vp, offs, nn,
+                              anc, out, Z, ws, ws_bytes, Z, Z)
+
+
+def test_attn_validation(L):
+    assert _attn(L, dt=7) == DTYPE
+    assert _attn(L, Hq=6, Hkv=4) == SHAPE
+    assert _attn(L, B=0) == SHAPE
+    assert _attn(L, n_max=65) == SHAPE
+    assert _attn(L, Lmax=-1) == SHAPE
+    assert _attn(L, D=96) == UNSUP
+    assert _attn(L, D=256) == UNSUP
+    assert _attn(L, dt=0, D=6) == UNSUP
+    assert _attn(L, dt=0, D=260) == UNSUP
+    assert _attn(L, q=Z) == NULL
+    assert _attn(L, anc=Z) == NULL
+    assert _attn(L, out=Z) == NULL
+    assert _attn(L, kp=Z) == NULL
+    assert _attn(L, q=ctypes.c_void_p(4098)) == UNSUP              # misaligned
+    assert _attn(L, ws=Z) == WS
+    need = L.tree_verify_attn_workspace_size(1, 2, 64, 8, 2, 128, 100)
+    assert need > 0
+    assert _attn(L, ws_bytes=need - 1) == WS
+
+
+def test_attn_workspace_size(L):
+    assert L.tree_verify_attn_workspace_size(0, 1, 10, 1, 1, 64, 32) == 0      # fp32 needs none
+    assert L.tree_verify_attn_workspace_size(1, 1, 64, 8, 3, 128, 10) == 0     # Hq % Hkv
+    big = L.tree_verify_attn_workspace_size(1, 4, 64, 64, 8, 128, 32768)
+    small = L.tree_verify_attn_workspace_size(1, 1, 64, 32, 32, 128, 2048)
+    assert big > 0 and small > 0
+    # one fp32 partial row of D plus (max, sum) per (sequence, node, head, chunk)
+    assert small % (64 * 32 * (128 * 4 + 8)) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libtreeverify.so")
+    with pytest.raises(ImportError):
+        _lib.lib()
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "tree_attention_verify_ancestor_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,328 @@
+"""HIP path against the oracle, through the C ABI, on the GPU.
+
+Integer outputs (bitsets, depths, positions, statuses, selected nodes, tokens,
+accepted lengths, paths) and the float32 expansion scores must match bit for bit;
+attention outputs must satisfy max|err| <= 2e-2 and max|err| <= 1e-2 * max|oracle|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention
+import synth
+import tree_attention_verify_ancestor_amd as tv
+from gpu_helpers import (DEV, anc_u64, attn_close, attn_device_inputs, dev_i32, dev_input,
+                         host, run_attn, run_expand)
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------- tree_build
+
+def _check_build(parent, n_nodes, prefix_len=None):
+    anc_r, dep_r, pos_r, st_r = oracle.tree_build(parent, n_nodes, prefix_len)
+    anc, dep, pos, st = tv.tree_build(dev_i32(parent), dev_i32(n_nodes),
+                                      None if prefix_len is None else dev_i32(prefix_len))
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), st_r)
+    assert np.array_equal(anc_u64(anc), anc_r)
+    assert np.array_equal(dep.cpu().numpy(), dep_r)
+    if prefix_len is not None:
+        assert np.array_equal(pos.cpu().numpy(), pos_r)
+
+
+def test_tree_build_static_workloads():
+    for wid in (1, 2):
+        w = synth.WORKLOADS[wid]
+        parent, nn = synth.static_tree(w)
+        _check_build(parent, nn, synth.prefix_lengths(w).astype(np.int32))
+
+
+@pytest.mark.parametrize("n_max", [64, 37, 1])
+def test_tree_build_random(n_max):
+    rng = np.random.default_rng(100 + n_max)
+    B = 257
+    parent = np.full((B, n_max), -1, dtype=np.int32)
+    nn = rng.integers(1, n_max + 1, size=B).astype(np.int32)
+    for b in range(B):
+        parent[b, :nn[b]] = synth.random_parents(rng, int(nn[b]), ["random", "chain", "star", "broom"][b % 4])
+        parent[b, nn[b]:] = rng.integers(-3, 70, size=n_max - nn[b])        # padding is ignored
+    _check_build(parent, nn, rng.integers(0, 100000, size=B).astype(np.int32))
+
+
+def test_tree_build_malformed():
+    cases = [([-1, 0, 1], 3), ([0, 0, 1], 3), ([-1, 0, 2], 3), ([-1, 2, 0], 3), ([-1, -5, 0], 3),
+             ([-1, 0, -1], 3), ([-1, -1, 7], 3), ([-1, 0, 1], 0), ([-1, 0, 1], 65), ([-1, 0, 1], -4),
+             ([-1] + [0] * 63, 64), ([-1, 0, 1, 2, 64], 5)]
+    parent = np.full((len(cases), 64), -1, dtype=np.int32)
+    nn = np.zeros(len(cases), dtype=np.int32)
+    for b, (p, n) in enumerate(cases):
+        parent[b, :len(p)] = p
+        nn[b] = n
+    _check_build(parent, nn, np.arange(len(cases), dtype=np.int32))
+
+
+# ----------------------------------------------------------------------------- tree_accept
+
+def _check_accept(parent, token, target, nn):
+    r = oracle.tree_accept(parent, token, target, nn)
+    par = dev_i32(parent)
+    d_nn = dev_i32(nn)
+    anc, depth, pos, st = tv.tree_build(par, d_nn)
+    got = tv.tree_accept(par, depth, anc, d_nn, dev_i32(token), dev_i32(target))
+    torch.cuda.synchronize()
+    for g, e, name in zip(got, r, ("accept_len", "best", "bonus", "path")):
+        assert np.array_equal(g.cpu().numpy(), e), name
+
+
+@pytest.mark.parametrize("vocab", [2, 3, 7, 32000])
+def test_accept_random(vocab):
+    rng = np.random.default_rng(200 + vocab)
+    B = 300
+    parent = np.full((B, 64), -1, dtype=np.int32)
+    nn = rng.integers(1, 65, size=B).astype(np.int32)
+    for b in range(B):
+        parent[b, :nn[b]] = synth.random_parents(rng, int(nn[b]), ["random", "chain", "star", "broom"][b % 4])
+    token = rng.integers(0, vocab, size=(B, 64)).astype(np.int32)
+    target = rng.integers(0, vocab, size=(B, 64)).astype(np.int32)
+    nn[::37] = 0                           # invalid trees give -1 everywhere
+    _check_accept(parent, token, target, nn)
+
+
+def test_accept_workload_targets():
+    for wid in (1, 2):
+        w = synth.WORKLOADS[wid]
+        parent, nn = synth.static_tree(w)
+        tok = synth.static_draft_tokens(w)
+        _check_accept(parent, tok, synth.target_ids(w, parent, tok, nn), nn)
+
+
+def test_accept_full_chain_and_no_match():
+    n = 64
+    parent = np.stack([synth.random_parents(None, n, "chain")] * 2)
+    token = np.stack([np.arange(100, 164, dtype=np.int32)] * 2)
+    target = np.stack([np.roll(token[0], -1), np.full(64, 7, np.int32)])
+    _check_accept(parent, token, target, np.array([n, n], np.int32))
+
+
+# ----------------------------------------------------------------------------- expansion
+
+def _check_expand(levels, k, m, roots, m_per_seq=None):
+    ref = oracle.expand_rerank(levels, k, m if m_per_seq is None else m_per_seq, roots)
+    out, fronts = run_expand(levels, k, m, roots, m_per_seq=m_per_seq)
+    st = out.seq_status.cpu().numpy()
+    assert np.array_equal(st, ref.status)
+    n = out.n_nodes.cpu().numpy()
+    assert np.array_equal(n, ref.n_nodes)
+    ok = ~ref.indeterminate
+    assert np.array_equal(out.parent.cpu().numpy()[ok], ref.parent[ok])
+    assert np.array_equal(out.token.cpu().numpy()[ok], ref.token[ok])
+    assert out.score.cpu().numpy()[ok].tobytes() == ref.score[ok].tobytes()
+    for s in range(len(levels)):
+        assert np.array_equal(fronts[s][ok], ref.frontier_tokens[s][ok]), f"frontier {s}"
+    return ref
+
+
+SMALL_EXPAND = [  # (B, k, S, V, m, quantised)
+    (3, 1, 4, 16, 64, True), (3, 2, 3, 16, 9, True), (4, 3, 3, 16, 64, True),
+    (2, 5, 4, 100, 30, False), (5, 8, 3, 1000, 64, False), (2, 10, 4, 777, 40, True),
+    (2, 16, 2, 4096, 64, False), (3, 4, 5, 33, 2, True), (2, 6, 6, 50, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_EXPAND)
+def test_expand_small(case):
+    B, k, S, V, m, quant = case
+    rng = np.random.default_rng(hash(case) % (2 ** 32))
+    levels = []
+    for s in range(S):
+        shape = (B, 1 if s == 0 else k, V)
+        if quant:
+            levels.append((rng.integers(-6, 7, size=shape) * 0.5).astype(np.float32))
+        else:
+            levels.append((rng.standard_normal(shape) * 2).astype(np.float32))
+    _check_expand(levels, k, m, rng.integers(0, V, size=B))
+
+
+def test_expand_nonfinite_and_m_per_seq():
+    rng = np.random.default_rng(7)
+    B, k, S, V = 4, 3, 3, 64
+    levels = [(rng.standard_normal((B, 1 if s == 0 else k, V)) * 2).astype(np.float32) for s in range(S)]
+    levels[1][1, 2, 11] = np.nan
+    levels[2][2, 0, 0] = np.inf
+    m_seq = np.array([5, 20, 64, 70], dtype=np.int32)          # the last is out of range
+    _check_expand(levels, k, 64, rng.integers(0, V, size=B), m_per_seq=m_seq)
+
+
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_expand_workload(wid):
+    w = synth.WORKLOADS[wid]
+    kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+    ref = _check_expand(synth.draft_logits(w), w.k, w.m if kc is None else 64,
+                        synth.root_tokens(w), m_per_seq=kc)
+    assert not ref.indeterminate.any()
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _check_attn(inp, parent, nn, what, lse_too=True):
+    ref, ref_lse = oracle.tree_verify_attn(inp.f32("q"), inp.f32("k_tree"), inp.f32("v_tree"),
+                                           inp.f32("k_prefix"), inp.f32("v_prefix"),
+                                           inp.prefix_offsets, parent, nn)
+    lens = np.diff(inp.prefix_offsets)
+    out, lse, st, _ = run_attn(attn_device_inputs(inp), parent, nn, int(lens.max()))
+    assert np.all(st.cpu().numpy() == 0)
+    ok, msg = attn_close(host(out), ref, what)
+    assert ok, msg
+    if lse_too:
+        err = np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse))
+        assert err <= 2e-2, f"{what} lse err {err}"
+    return out, lse
+
+
+SMALL_ATTN = [  # (B, Hq, Hkv, D, prefix lengths, node counts)
+    (1, 1, 1, 128, (0,), (1,)),
+    (1, 2, 2, 128, (1,), (10,)),
+    (2, 8, 2, 128, (63, 65), (33, 64)),
+    (3, 32, 8, 128, (300, 1, 777), (60, 7, 64)),
+    (2, 8, 1, 128, (1000, 2049), (64, 17)),
+    (4, 4, 4, 64, (129, 0, 64, 511), (26, 64, 1, 40)),
+    (2, 16, 2, 64, (5000, 300), (64, 50)),
+    (1, 32, 32, 128, (2048,), (26,)),
+    (5, 64, 8, 128, (700, 10, 1500, 64, 0), (64, 3, 64, 32, 64)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_ATTN)
+def test_attn_small_bf16(case):
+    B, Hq, Hkv, D, lens, ns = case
+    inp, parent, nn = synth.random_attention_case(abs(hash(case)) % 10000, B, Hq, Hkv, D, lens, ns,
+                                                  dtype="bf16", std=0.5)
+    _check_attn(inp, parent, nn, f"case {case}")
+
+
+@pytest.mark.parametrize("std", [0.5, 2.0])
+def test_attn_fp32(std):
+    inp, parent, nn = synth.random_attention_case(17, 3, 4, 2, 64, (32, 0, 333), (10, 64, 5),
+                                                  dtype="f32", std=std)
+    _check_attn(inp, parent, nn, "fp32")
+
+
+def test_attn_tiny_workload():
+    w = synth.WORKLOADS[1]
+    parent, nn = synth.static_tree(w)
+    _check_attn(synth.attention_inputs(w), parent, nn, "workload 1")
+
+
+@pytest.mark.parametrize("G,L", [(1, 100), (4, 0), (8, 3000)])
+def test_attn_one_hot_mask_exact(G, L):
+    """Tree V rows are unit vectors e_j and prefix V is 0 in the first 64 coordinates,
+    so out[i][h][j] must be exactly 0 for j off i's root path and > 0 on it."""
+    Hkv = 2
+    inp, parent, nn = synth.random_attention_case(31 + G, 2, G * Hkv, Hkv, 128, (L, L // 2 + 1),
+                                                  (64, 45), dtype="bf16", std=0.5)
+    one = synth.bf16_bits(np.float32([1.0]))[0]
+    inp.v_tree[:] = 0
+    for j in range(64):
+        inp.v_tree[:, j, :, j] = one
+    inp.v_prefix[:, :, :64] = 0
+    anc, _, _, _ = oracle.tree_build(parent, nn, None)
+    out, _, _, _ = run_attn(attn_device_inputs(inp), parent, nn, int(np.diff(inp.prefix_offsets).max()))
+    o = host(out)
+    for b in range(2):
+        for i in range(int(nn[b])):
+            on = np.array([(int(anc[b, i]) >> j) & 1 for j in range(64)], dtype=bool)
+            on[int(nn[b]):] = False
+            blk = o[b, i, :, :64]
+            assert np.all(blk[:, ~on] == 0.0), (b, i)
+            assert np.all(blk[:, on] > 0.0), (b, i)
+    assert np.all(o[1, int(nn[1]):] == 0.0)
+
+
+def test_attn_deterministic():
+    inp, parent, nn = synth.random_attention_case(5, 3, 32, 8, 128, (3000, 100, 4097), (64, 20, 50))
+    d = attn_device_inputs(inp)
+    a1, l1, _, _ = run_attn(d, parent, nn, 4097)
+    a2, l2, _, _ = run_attn(d, parent, nn, 4097)
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_attn_workload2_full():
+    w = synth.WORKLOADS[2]
+    parent, nn = synth.static_tree(w)
+    _check_attn(synth.attention_inputs(w), parent, nn, "workload 2")
+
+
+def test_attn_workload3_full():
+    w = synth.WORKLOADS[3]
+    ref = oracle.expand_rerank(synth.draft_logits(w), w.k, w.m, synth.root_tokens(w))
+    _check_attn(synth.attention_inputs(w), ref.parent, ref.n_nodes, "workload 3")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wid", [4, 5])
+def test_attn_workload_sampled(wid):
+    """Full-size workloads 4 and 5 in the bench's launch configuration; the oracle
+    recomputes a seeded sample of output rows one by one."""
+    w = synth.WORKLOADS[wid]
+    kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+    tree = oracle.expand_rerank(synth.draft_logits(w), w.k, w.m if kc is None else kc,
+                                synth.root_tokens(w))
+    inp = synth.attention_inputs(w)
+    lens = np.diff(inp.prefix_offsets)
+    out, lse, st, _ = run_attn(attn_device_inputs(inp), tree.parent, tree.n_nodes, int(lens.max()))
+    assert np.all(st.cpu().numpy() == 0)
+    o = host(out)
+    l = lse.cpu().numpy()
+    rng = np.random.default_rng(wid)
+    picks = {}
+    for _ in range(48):
+        b = int(rng.integers(0, w.B))
+        picks.setdefault(b, []).append((int(rng.integers(0, w.Hq)), int(rng.integers(0, tree.n_nodes[b]))))
+    for b, hi in picks.items():
+        o0, o1 = int(inp.prefix_offsets[b]), int(inp.prefix_offsets[b + 1])
+        one = dict(q=synth.bf16_to_f32(inp.q[b:b + 1]),
+                   k_tree=synth.bf16_to_f32(inp.k_tree[b:b + 1]),
+                   v_tree=synth.bf16_to_f32(inp.v_tree[b:b + 1]),
+                   k_prefix=synth.bf16_to_f32(inp.k_prefix[o0:o1]),
+                   v_prefix=synth.bf16_to_f32(inp.v_prefix[o0:o1]))
+        offs = np.array([0, o1 - o0], dtype=np.int64)
+        for h, i in hi:
+            ref, ref_l = oracle.attention.tree_verify_attn_one(
+                one["q"], one["k_tree"], one["v_tree"], one["k_prefix"], one["v_prefix"], offs,
+                tree.parent[b:b + 1], 0, h, i)
+            ok, msg = attn_close(o[b, i, h], ref, f"workload {wid} b={b} h={h} i={i}")
+            assert ok, msg
+            assert abs(float(l[b, i, h]) - ref_l) <= 2e-2
+    # padding rows are zero
+    for b in range(w.B):
+        assert np.all(o[b, int(tree.n_nodes[b]):] == 0.0)
+
+
+# ----------------------------------------------------------------------------- whole path
+
+def test_pipeline_workload3():
+    """expand x S -> tree_build -> tree_verify_attn -> tree_accept, all on the GPU."""
+    w = synth.WORKLOADS[3]
+    levels = synth.draft_logits(w)
+    roots = synth.root_tokens(w)
+    ref_tree = oracle.expand_rerank(levels, w.k, w.m, roots)
+    out, _ = run_expand(levels, w.k, w.m, roots)
+    anc, depth, pos, st = tv.tree_build(out.parent, out.n_nodes)
+    inp = synth.attention_inputs(w)
+    d = attn_device_inputs(inp)
+    att, lse, ast = tv.tree_verify_attn(d["q"], d["k_tree"], d["v_tree"], d["k_prefix"],
+                                        d["v_prefix"], d["offsets"], out.n_nodes, anc, w.prefix)
+    tgt = synth.target_ids(w, ref_tree.parent, ref_tree.token, ref_tree.n_nodes)
+    acc = tv.tree_accept(out.parent, depth, anc, out.n_nodes, out.token, dev_i32(tgt))
+    torch.cuda.synchronize()
+    ref_attn, _ = oracle.tree_verify_attn(inp.f32("q"), inp.f32("k_tree"), inp.f32("v_tree"),
+                                          inp.f32("k_prefix"), inp.f32("v_prefix"),
+                                          inp.prefix_offsets, ref_tree.parent, ref_tree.n_nodes)
+    ok, msg = attn_close(host(att), ref_attn, "pipeline")
+    assert ok, msg
+    ref_acc = oracle.tree_accept(ref_tree.parent, ref_tree.token, tgt, ref_tree.n_nodes)
+    for g, e in zip(acc, ref_acc):
+        assert np.array_equal(g.cpu().numpy(), e)
