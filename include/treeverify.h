@@ -1,0 +1,199 @@
+/*
+ * treeverify -- draft-tree verification for EAGLE-style speculative decoding on
+ * AMD MI355X (gfx950).  C ABI of the library libtreeverify.so.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [EAGLE]    "EAGLE" study notes on EAGLE-1/2/3 (s1mplewind astro-blog): sections
+ *              "1. EAGLE pipeline / Draft Model", "3. Verify", "Well-Calibrated Draft
+ *              Model", "Expansion of tree", "Reranking Nodes".
+ *   [EAGLE-3]  "What is EAGLE-3 and how does it differ from standard speculative
+ *              decoding?" (aivaro.ru Q&A): section 3 (tree attention term) and
+ *              section 4, step 4 "Accepting the sequence".
+ *   [EAGLE-4]  "Technical analysis of EAGLE-4" (dev48.org translation): section
+ *              "EAGLE-4 verification trees and the harness".
+ *
+ * Conventions shared by every call
+ *   - A draft tree holds at most TV_MAX_NODES = 64 nodes, the root included.  Node 0
+ *     is the root: the token the target emitted last, queried in this pass but not
+ *     yet in the KV cache.  parent[0] == -1 and 0 <= parent[i] < i for i >= 1.
+ *   - Per-sequence arrays are [B][n_max] row-major with 1 <= n_max <= 64; entries at
+ *     or beyond n_nodes[b] are padding.
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except where a
+ *     comment says host.  The library allocates nothing and keeps no state between
+ *     calls: workspaces are caller-owned and sized by the *_workspace_size queries.
+ *   - Every call validates its host-side arguments first and returns an error
+ *     status without touching the device when they are wrong.  Otherwise it only
+ *     enqueues kernels on `stream` (asynchronous; no host synchronisation) and
+ *     returns TV_OK, or TV_ERR_HIP if the launch itself failed.
+ *   - Errors found in device data are reported per sequence in seq_status[b] (when
+ *     the pointer is not NULL) with the TV_SEQ_* codes below; the outputs of that
+ *     sequence are then zeros / -1 and the other sequences are unaffected.  No
+ *     kernel reads or writes outside the buffers described, whatever the data.
+ *   - Calls on one stream are ordered; calls that share output or workspace
+ *     buffers must not run concurrently on different streams.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_ABI_VERSION 1
+#define TV_MAX_NODES 64
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_NULL = 1,         /* a required pointer is NULL */
+  TV_ERR_SHAPE = 2,        /* a size argument is out of range or inconsistent */
+  TV_ERR_DTYPE = 3,        /* unknown tv_dtype */
+  TV_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement (e.g. head_dim) */
+  TV_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the size query returns */
+  TV_ERR_HIP = 6           /* the HIP runtime reported an error when launching */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* per-sequence device status codes written to seq_status[b] */
+#define TV_SEQ_OK 0
+#define TV_SEQ_BAD_PARENT 1   /* parent[0] != -1, or parent[i] < -1, or parent[i] >= i */
+#define TV_SEQ_SECOND_ROOT 2  /* parent[i] == -1 for some i >= 1 */
+#define TV_SEQ_BAD_N 3        /* n_nodes (or the kept count m) outside [1, n_max] */
+#define TV_SEQ_NONFINITE 4    /* a draft-logit row holds NaN or +-Inf */
+#define TV_SEQ_BAD_PREFIX 5   /* prefix_offsets[b+1] - prefix_offsets[b] outside [0, max_prefix_len] */
+#define TV_SEQ_BAD_STATE 6    /* expansion step called out of order for this workspace */
+
+int tv_abi_version(void);
+const char* tv_status_string(tv_status s);
+
+/*
+ * tree_build -- structure of each draft tree.
+ * [EAGLE] "1. EAGLE pipeline / Draft Model": the draft is a tree of depth m holding
+ * more than m tokens.  [EAGLE-4] "verification trees": a node may see the prefix,
+ * its ancestors and itself; this call turns the parent array into that visibility.
+ *
+ *   parent     int32 [B][n_max]   in
+ *   n_nodes    int32 [B]          in   nodes per tree, root included
+ *   prefix_len int32 [B]          in   nullable (then 0)
+ *   anc        uint64 [B][n_max]  out  bit j of anc[b][i] set iff node j lies on the
+ *                                      path root -> i (root and i included)
+ *   depth      int32 [B][n_max]   out  parent steps from i to the root
+ *   pos        int32 [B][n_max]   out  nullable; prefix_len + depth, the position the
+ *                                      caller encodes node i at
+ *   seq_status int32 [B]          out  nullable; TV_SEQ_BAD_PARENT / SECOND_ROOT /
+ *                                      BAD_N, the first offending node deciding
+ * Padding entries and failed sequences hold anc 0, depth -1, pos -1.
+ */
+tv_status tree_build(int B, int n_max, const int32_t* parent, const int32_t* n_nodes,
+                     const int32_t* prefix_len, uint64_t* anc, int32_t* depth, int32_t* pos,
+                     int32_t* seq_status, hipStream_t stream);
+
+/*
+ * tree_expand_rerank -- one level of EAGLE-2 dynamic tree construction.
+ * [EAGLE] "Well-Calibrated Draft Model": a draft token's confidence is the softmax of
+ * the draft logits.  "Expansion of tree": a node's value is the product of the
+ * confidences on its root path; the top-k are kept.  "Reranking Nodes": the m nodes
+ * of largest value over everything generated form the tree that is verified.
+ *
+ * Call once per level, step = 1 .. max_steps, in order, with the same workspace
+ * (step 1 resets it).  Per sequence, the frontier of a level is a list of k nodes
+ * ranked best first; at step 1 it is the root alone.
+ *   logits fp32 [B][rows][vocab], rows = 1 at step 1 and k after; row r holds the
+ *          draft logits of the frontier node of rank r.
+ * For every row: lse = log-sum-exp of the row, computed in float64 from the max and
+ * rounded once to float32; the k tokens of largest logit (ties to the lower id)
+ * become children with score = fl32(parent score + fl32(logit - lse)), the summed
+ * log-confidence (log of the value).  Children are numbered in creation order
+ * (row, then top-k rank).  The next frontier is the k best children of this level
+ * by (score descending, creation ascending).
+ * When final_m > 0 (the last level), the whole pool of children is reranked: the
+ * m - 1 best by the same order are kept with the root (m = m_per_seq[b] if that
+ * pointer is given, else final_m), and written root first, then by (depth,
+ * creation), with parents remapped to output indices:
+ *   parent int32 [B][n_max], token int32 [B][n_max] (token[b][0] = root_token[b]),
+ *   score fp32 [B][n_max] (root 0), n_nodes int32 [B]; padding -1 / -1 / 0.
+ * frontier_token int32 [B][k] (nullable) receives the tokens of the new frontier by
+ * rank at every step, for the caller's next draft pass.
+ * Limits: 1 <= k <= 16, k <= vocab, max_steps >= 1, k + (max_steps-1)*k*k <= 4096,
+ * 1 <= n_max <= 64, 0 <= final_m <= n_max.  root_token may be NULL unless final_m > 0.
+ * Device errors: TV_SEQ_NONFINITE (sticky for later steps), TV_SEQ_BAD_N (m), and
+ * TV_SEQ_BAD_STATE (step > 1 without the previous step on this workspace).
+ */
+size_t tree_expand_workspace_size(int B, int k, int max_steps);
+tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int max_steps, int step,
+                             int vocab, const float* logits, int final_m, const int32_t* m_per_seq,
+                             const int32_t* root_token, int n_max, int32_t* parent, int32_t* token,
+                             float* score, int32_t* n_nodes, int32_t* frontier_token,
+                             int32_t* seq_status, hipStream_t stream);
+
+/*
+ * tree_verify_attn -- tree-masked attention of one target layer over all draft nodes.
+ * [EAGLE-4] "verification trees": each token attends to the shared prefix, its
+ * ancestors and itself; siblings and other branches stay hidden.  [EAGLE] "3. Verify"
+ * and [EAGLE-3] section 3: all branches are checked in one target forward pass.
+ *
+ * For sequence b, query head h, node i < n_nodes[b], with g = h / (Hq / Hkv):
+ *   out[b][i][h] = sum_j softmax_j(scale * q . k_j) v_j over the keys
+ *   j in { prefix 0 .. L_b-1 of kv head g } U { tree nodes j with bit j of anc[b][i] }
+ *   lse[b][i][h] = natural-log log-sum-exp of those scores (nullable output).
+ * Layouts (element type per dt; all contiguous, row-major):
+ *   q              [B][n_max][Hq][D]
+ *   k_tree, v_tree [B][n_max][Hkv][D]   K/V of the tree nodes from this pass
+ *   k_prefix, v_prefix [total][Hkv][D]  cached prefix, sequences packed back to back:
+ *                  sequence b owns rows prefix_offsets[b] .. prefix_offsets[b+1]-1
+ *   prefix_offsets int64 [B+1]          L_b = offsets[b+1] - offsets[b] <= max_prefix_len
+ *   n_nodes int32 [B], anc uint64 [B][n_max] (from tree_build)
+ *   out            [B][n_max][Hq][D]    rows of padding nodes and failed sequences are 0
+ *   lse fp32       [B][n_max][Hq]       nullable; 0 where out is 0
+ * scale <= 0 selects 1/sqrt(D).  Supported: dt = TV_BF16 with D in {64, 128}
+ * (fp32 accumulation, bf16 output, round to nearest even) and dt = TV_F32 with
+ * D % 4 == 0 and D <= 256.  k_prefix / v_prefix may be NULL when max_prefix_len == 0.
+ * ws: caller workspace of tree_verify_attn_workspace_size(...) bytes for the split-KV
+ * partial results (may be NULL when that size is 0).  Device errors: TV_SEQ_BAD_N,
+ * TV_SEQ_BAD_PREFIX in seq_status (nullable).
+ */
+size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
+                                       int max_prefix_len);
+tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max,
+                           int max_prefix_len, float scale, const void* q, const void* k_tree,
+                           const void* v_tree, const void* k_prefix, const void* v_prefix,
+                           const int64_t* prefix_offsets, const int32_t* n_nodes,
+                           const uint64_t* anc, void* out, float* lse, void* ws, size_t ws_bytes,
+                           int32_t* seq_status, hipStream_t stream);
+
+/*
+ * tree_accept -- greedy acceptance of the longest matching path.
+ * [EAGLE] "Well-Calibrated Draft Model": under greedy decoding a draft token is
+ * accepted when it is the target's most likely token.  [EAGLE-3] section 4 step 4:
+ * the target keeps the longest prefix of the tree whose tokens all pass.  [EAGLE-4]
+ * "verification trees": after the accepted path, generation continues with the
+ * target's own token.
+ *
+ *   parent, depth int32 [B][n_max], anc uint64 [B][n_max], n_nodes int32 [B]
+ *                  (a tree that tree_build accepted)
+ *   token          int32 [B][n_max]  draft token of each node (token[b][0] is the root's)
+ *   target_next    int32 [B][n_max]  the target's greedy token after node i
+ *   accept_len     int32 [B]  out    depth of the chosen node (accepted draft tokens)
+ *   best_node      int32 [B]  out    the deepest node whose root path all passes
+ *                                    (node j >= 1 passes iff token[j] ==
+ *                                    target_next[parent[j]]); ties to the lowest index
+ *   bonus_token    int32 [B]  out    target_next[best_node]
+ *   path           int32 [B][n_max] out, nullable: the chosen path without the root in
+ *                                    index order, -1 padded
+ * Sequences with n_nodes outside [1, n_max], or whose anc[b][0] != 1 (a tree
+ * tree_build rejected), get -1 in every output.
+ */
+tv_status tree_accept(int B, int n_max, const int32_t* parent, const int32_t* depth,
+                      const uint64_t* anc, const int32_t* n_nodes, const int32_t* token,
+                      const int32_t* target_next, int32_t* accept_len, int32_t* best_node,
+                      int32_t* bonus_token, int32_t* path, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

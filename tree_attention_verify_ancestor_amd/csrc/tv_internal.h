@@ -1,0 +1,47 @@
+// Internal helpers shared by the treeverify HIP sources (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "treeverify.h"
+
+#define TV_API extern "C" __attribute__((visibility("default")))
+
+namespace tv {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl((uint32_t)v, src);
+  uint32_t hi = __shfl((uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = shfl_u64(v, lane_id() ^ o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Host-side launch check.
+inline tv_status launch_status() {
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+}  // namespace tv

@@ -1,0 +1,171 @@
+"""Python binding of the treeverify C ABI: argument marshalling only.
+
+Every function takes torch tensors already on the GPU, checks their dtype, shape and
+layout, allocates the outputs it returns with torch (device memory is torch's job),
+and calls the library on torch's current stream.  All arithmetic of every step runs
+in the HIP kernels of libtreeverify.so; nothing here computes on the host.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+_DT = {torch.float32: _lib.TV_F32, torch.bfloat16: _lib.TV_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def abi_version():
+    return lib().tv_abi_version()
+
+
+def tree_build(parent, n_nodes, prefix_len=None, with_pos=True):
+    """(anc int64 [B][n_max] holding the uint64 bit patterns, depth, pos, seq_status)."""
+    _need(parent, "parent", torch.int32, 2)
+    B, n_max = parent.shape
+    _need(n_nodes, "n_nodes", torch.int32, shape=(B,))
+    if prefix_len is not None:
+        _need(prefix_len, "prefix_len", torch.int32, shape=(B,))
+    dev = parent.device
+    anc = torch.empty((B, n_max), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    pos = torch.empty((B, n_max), dtype=torch.int32, device=dev) if with_pos else None
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    check("tree_build", lib().tree_build(B, n_max, _ptr(parent), _ptr(n_nodes), _ptr(prefix_len),
+                                         _ptr(anc), _ptr(depth), _ptr(pos), _ptr(status),
+                                         _stream()))
+    return anc, depth, pos, status
+
+
+def expand_workspace(B, k, max_steps, device="cuda"):
+    n = lib().tree_expand_workspace_size(B, k, max_steps)
+    if n == 0:
+        raise ValueError(f"unsupported expansion shape B={B} k={k} max_steps={max_steps}")
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+class ExpandOutputs:
+    """Outputs of the last expansion level (tree in output order) plus per-call state."""
+
+    def __init__(self, B, n_max, k, device):
+        self.parent = torch.empty((B, n_max), dtype=torch.int32, device=device)
+        self.token = torch.empty((B, n_max), dtype=torch.int32, device=device)
+        self.score = torch.empty((B, n_max), dtype=torch.float32, device=device)
+        self.n_nodes = torch.empty((B,), dtype=torch.int32, device=device)
+        self.frontier_token = torch.empty((B, k), dtype=torch.int32, device=device)
+        self.seq_status = torch.empty((B,), dtype=torch.int32, device=device)
+
+
+def tree_expand_rerank(ws, step, logits, k, max_steps, final_m=0, m_per_seq=None,
+                       root_token=None, n_max=64, out=None):
+    """One EAGLE-2 level.  logits: fp32 [B][1 if step == 1 else k][vocab]."""
+    _need(ws, "ws", torch.uint8, 1)
+    _need(logits, "logits", torch.float32, 3)
+    B, rows, vocab = logits.shape
+    if rows != (1 if step == 1 else k):
+        raise ValueError(f"step {step} needs {1 if step == 1 else k} logit rows, got {rows}")
+    if m_per_seq is not None:
+        _need(m_per_seq, "m_per_seq", torch.int32, shape=(B,))
+    if root_token is not None:
+        _need(root_token, "root_token", torch.int32, shape=(B,))
+    if out is None:
+        out = ExpandOutputs(B, n_max, k, logits.device)
+    check("tree_expand_rerank", lib().tree_expand_rerank(
+        _ptr(ws), ws.numel(), B, k, max_steps, step, vocab, _ptr(logits), final_m,
+        _ptr(m_per_seq), _ptr(root_token), n_max, _ptr(out.parent), _ptr(out.token),
+        _ptr(out.score), _ptr(out.n_nodes), _ptr(out.frontier_token), _ptr(out.seq_status),
+        _stream()))
+    return out
+
+
+def attn_workspace(dtype, B, n_max, Hq, Hkv, D, max_prefix_len, device="cuda"):
+    n = lib().tree_verify_attn_workspace_size(_DT[dtype], B, n_max, Hq, Hkv, D, max_prefix_len)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+
+
+def tree_verify_attn(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, n_nodes, anc,
+                     max_prefix_len, scale=0.0, out=None, lse=None, ws=None, seq_status=None,
+                     want_lse=True):
+    """Tree-masked attention.  q [B][n_max][Hq][D]; tree K/V [B][n_max][Hkv][D];
+    prefix K/V packed [total][Hkv][D] with int64 offsets [B+1]; anc int64 [B][n_max]."""
+    if q.dtype not in _DT:
+        raise TypeError(f"q must be float32 or bfloat16, got {q.dtype}")
+    dt = q.dtype
+    _need(q, "q", dt, 4)
+    B, n_max, Hq, D = q.shape
+    _need(k_tree, "k_tree", dt, 4)
+    Hkv = k_tree.shape[2]
+    _need(k_tree, "k_tree", dt, shape=(B, n_max, Hkv, D))
+    _need(v_tree, "v_tree", dt, shape=(B, n_max, Hkv, D))
+    _need(k_prefix, "k_prefix", dt, 3)
+    _need(v_prefix, "v_prefix", dt, shape=tuple(k_prefix.shape))
+    if k_prefix.shape[1:] != (Hkv, D):
+        raise ValueError(f"k_prefix must be [total][{Hkv}][{D}], got {tuple(k_prefix.shape)}")
+    _need(prefix_offsets, "prefix_offsets", torch.int64, shape=(B + 1,))
+    _need(n_nodes, "n_nodes", torch.int32, shape=(B,))
+    _need(anc, "anc", torch.int64, shape=(B, n_max))
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, n_max, Hq, D), dtype=dt, device=dev)
+    _need(out, "out", dt, shape=(B, n_max, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_max, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, n_max, Hq))
+    if ws is None:
+        ws = attn_workspace(dt, B, n_max, Hq, Hkv, D, max_prefix_len, dev)
+    if seq_status is None:
+        seq_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    check("tree_verify_attn", lib().tree_verify_attn(
+        _DT[dt], B, Hq, Hkv, D, n_max, int(max_prefix_len), float(scale), _ptr(q), _ptr(k_tree),
+        _ptr(v_tree), _ptr(kp), _ptr(vp), _ptr(prefix_offsets), _ptr(n_nodes), _ptr(anc),
+        _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _ptr(seq_status), _stream()))
+    return out, lse, seq_status
+
+
+def tree_accept(parent, depth, anc, n_nodes, token, target_next, want_path=True):
+    """(accept_len, best_node, bonus_token, path) -- int32 tensors."""
+    _need(parent, "parent", torch.int32, 2)
+    B, n_max = parent.shape
+    _need(depth, "depth", torch.int32, shape=(B, n_max))
+    _need(anc, "anc", torch.int64, shape=(B, n_max))
+    _need(n_nodes, "n_nodes", torch.int32, shape=(B,))
+    _need(token, "token", torch.int32, shape=(B, n_max))
+    _need(target_next, "target_next", torch.int32, shape=(B, n_max))
+    dev = parent.device
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    best = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    path = torch.empty((B, n_max), dtype=torch.int32, device=dev) if want_path else None
+    check("tree_accept", lib().tree_accept(B, n_max, _ptr(parent), _ptr(depth), _ptr(anc),
+                                           _ptr(n_nodes), _ptr(token), _ptr(target_next),
+                                           _ptr(alen), _ptr(best), _ptr(bonus), _ptr(path),
+                                           _stream()))
+    return alen, best, bonus, path
