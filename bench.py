@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Throughput of the draft-tree verification hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  dynamic-tree workloads: tree_expand_rerank for every level (rerank on the last),
+  then tree_build, tree_verify_attn and tree_accept;
+  static-tree workloads:  tree_build, tree_verify_attn and tree_accept.
+The metric is node.head queries per second (sum over sequences of n_nodes * Hq per
+step, divided by the step time).  Inputs are resident in HBM before timing starts;
+each step reads its own copy of every input, rotating over enough copies (>= 1 GiB)
+that the 256 MiB last-level cache cannot serve repeated reads.
+
+Each step is captured once per input copy into a HIP graph (so host launch cost is
+not what is timed) and the graphs are replayed.  The dominant kernel's roofline uses
+the tree_verify_attn call: its algorithmic bytes (prefix K/V + tree K/V + Q + O)
+divided by its average duration, measured with HIP events on its stream around
+graph replays of back-to-back attention calls over the rotated copies.  The CPU
+baseline is the plain oracle timed on a bounded sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify attn: node·head queries/s; KV HBM GB/s as % of peak"
+UNIT = "node·head queries/s"
+HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0           # MI355X dense bf16
+DEFAULT_WORKLOAD = 2                     # the Llama-7B-shaped MHA layer with a static tree
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bounded CPU work for the oracle baseline (0 disables it)")
+    ap.add_argument("--attn-reps", type=int, default=20,
+                    help="replays of the back-to-back attention graph for the kernel timing")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the attention kernel source; recorded counter traffic is valid only for it."""
+    p = os.path.join(ROOT, "tree_attention_verify_ancestor_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload_name):
+    """Counter-measured HBM bytes per attention launch from profiles/, if still valid."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(workload_name)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("attn_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Inputs:
+    """Host-side synthetic inputs of one workload (numpy), shared by GPU and CPU legs."""
+
+    def __init__(self, w):
+        import synth
+        self.w = w
+        self.attn = synth.attention_inputs(w)
+        self.lens = np.diff(self.attn.prefix_offsets)
+        self.dynamic = not isinstance(w.tree, list)
+        if self.dynamic:
+            self.levels = synth.draft_logits(w)
+            self.roots = synth.root_tokens(w)
+            self.m_seq = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+        else:
+            self.parent, self.n_nodes = synth.static_tree(w)
+            self.tokens = synth.static_draft_tokens(w)
+            self.target = synth.target_ids(w, self.parent, self.tokens, self.n_nodes)
+
+    def algorithmic_bytes(self, n_nodes):
+        """Prefix K/V + tree K/V + Q + O bytes of one attention launch."""
+        w = self.w
+        el = 2 if w.dtype == "bf16" else 4
+        prefix = int(self.lens.sum()) * w.Hkv * w.D * 2 * el
+        nodes = int(np.sum(n_nodes))
+        tree = nodes * w.Hkv * w.D * 2 * el
+        qo = nodes * w.Hq * w.D * 2 * el
+        return prefix + tree + qo
+
+    def algorithmic_flops(self, parent, n_nodes):
+        """2*D multiply-adds for QK and for PV per visible (query row, key) pair."""
+        w = self.w
+        tot = 0
+        for b in range(w.B):
+            n = int(n_nodes[b])
+            depth_sum = 0
+            for i in range(n):
+                d, j = 0, i
+                while j > 0:
+                    j = int(parent[b, j])
+                    d += 1
+                depth_sum += d + 1
+            tot += (n * int(self.lens[b]) + depth_sum) * w.Hq
+        return 4.0 * w.D * tot
+
+
+def gpu_leg(args, inp):
+    import torch
+    import synth
+    import tree_attention_verify_ancestor_amd as tv
+
+    w = inp.w
+    dev = "cuda"
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    per_copy = inp.algorithmic_bytes(np.full(w.B, w.n_max)) + sum(
+        lv.nbytes for lv in getattr(inp, "levels", []))
+    R = max(2, math.ceil(ROTATE_BYTES / per_copy))
+    base = dict(q=to_dev(inp.attn.q), k_tree=to_dev(inp.attn.k_tree), v_tree=to_dev(inp.attn.v_tree),
+                k_prefix=to_dev(inp.attn.k_prefix), v_prefix=to_dev(inp.attn.v_prefix))
+    offsets = torch.from_numpy(inp.attn.prefix_offsets).to(dev)
+    prefix_len = i32(inp.lens)
+    copies = []
+    for r in range(R):
+        c = {k: v.clone() for k, v in base.items()}
+        if inp.dynamic:
+            c["levels"] = [torch.from_numpy(lv).to(dev) for lv in inp.levels]
+            c["ws"] = tv.expand_workspace(w.B, w.k, w.S, dev)
+            c["exp"] = tv.ExpandOutputs(w.B, w.n_max, w.k, dev)
+        copies.append(c)
+    del base
+    max_prefix = int(inp.lens.max())
+    attn_ws = tv.attn_workspace(dt, w.B, w.n_max, w.Hq, w.Hkv, w.D, max_prefix, dev)
+    roots = i32(inp.roots) if inp.dynamic else None
+    m_seq = i32(inp.m_seq) if inp.dynamic and inp.m_seq is not None else None
+    if not inp.dynamic:
+        parent_d, nn_d = i32(inp.parent), i32(inp.n_nodes)
+        tok_d, tgt_d = i32(inp.tokens), i32(inp.target)
+
+    def tree_of(c):
+        if not inp.dynamic:
+            return parent_d, nn_d, tok_d
+        e = c["exp"]
+        for s in range(w.S):
+            final = (64 if m_seq is not None else w.m) if s == w.S - 1 else 0
+            tv.tree_expand_rerank(c["ws"], s + 1, c["levels"][s], w.k, w.S, final_m=final,
+                                  m_per_seq=m_seq, root_token=roots, n_max=w.n_max, out=e)
+        return e.parent, e.n_nodes, e.token
+
+    def attention(c, nn, anc):
+        return tv.tree_verify_attn(c["q"], c["k_tree"], c["v_tree"], c["k_prefix"], c["v_prefix"],
+                                   offsets, nn, anc, max_prefix, ws=attn_ws)
+
+    if inp.dynamic:
+        # target ids follow the built tree (input preparation, outside any timing)
+        par, nn, tok = tree_of(copies[0])
+        torch.cuda.synchronize()
+        tgt_d = i32(synth.target_ids(w, par.cpu().numpy(), tok.cpu().numpy(), nn.cpu().numpy()))
+        tree_host = (par.cpu().numpy(), nn.cpu().numpy())
+    else:
+        tree_host = (inp.parent, inp.n_nodes)
+
+    def step(c):
+        par, nn, tok = tree_of(c)
+        anc, depth, pos, st = tv.tree_build(par, nn, prefix_len)
+        out, lse, ast = attention(c, nn, anc)
+        acc = tv.tree_accept(par, depth, anc, nn, tok, tgt_d)
+        return out, lse, acc
+
+    # eager warm-up (allocator, code objects), then one graph per input copy
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in copies[:2]:
+            step(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs, keep = [], []
+    for c in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            keep.append(step(c))
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms_events = e0.elapsed_time(e1) / args.steps
+    step_ms_wall = (t1 - t0) * 1e3 / args.steps
+
+    # attention launches back to back over the rotated copies
+    anc_nn = []
+    for c in copies:
+        par, nn, _ = tree_of(c)
+        anc, _, _, _ = tv.tree_build(par, nn, prefix_len)
+        anc_nn.append((nn, anc))
+    torch.cuda.synchronize()
+    ag = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for c, (nn, anc) in zip(copies, anc_nn):
+            attention(c, nn, anc)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(ag):
+        att_keep = [attention(c, nn, anc) for c, (nn, anc) in zip(copies, anc_nn)]
+    ag.replay()
+    torch.cuda.synchronize()
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.attn_reps):
+        ag.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / (args.attn_reps * R)
+    return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, copies=R,
+                tree=tree_host)
+
+
+def cpu_leg(args, inp, tree):
+    """The oracle as it stands, on the host cores, over a bounded number of steps."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits, threadpool_info
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return _cpu_steps(args, inp, oracle, synth, blas)
+
+
+def _cpu_steps(args, inp, oracle, synth, blas):
+    w = inp.w
+    a = inp.attn
+    q, kt, vt = a.f32("q"), a.f32("k_tree"), a.f32("v_tree")
+    kp, vp = a.f32("k_prefix"), a.f32("v_prefix")
+    # target ids for the accept step (input preparation, not timed)
+    tgts = {}
+    for b in range(min(w.B, 64)):
+        if inp.dynamic:
+            res = oracle.expand_rerank([lv[b:b + 1] for lv in inp.levels], w.k,
+                                       w.m if inp.m_seq is None else inp.m_seq[b:b + 1],
+                                       inp.roots[b:b + 1])
+            tgts[b] = synth.target_ids(w, res.parent, res.token, res.n_nodes)
+        else:
+            tgts[b] = inp.target[b:b + 1]
+    steps = 0
+    queries = 0
+    t0 = time.perf_counter()
+    # whole steps on the first sequences until the time budget is spent
+    order = list(range(w.B))
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        b = order[steps % min(w.B, 64)]
+        if inp.dynamic:
+            res = oracle.expand_rerank([lv[b:b + 1] for lv in inp.levels], w.k,
+                                       w.m if inp.m_seq is None else inp.m_seq[b:b + 1],
+                                       inp.roots[b:b + 1])
+            par, nn, tok = res.parent, res.n_nodes, res.token
+        else:
+            par, nn, tok = inp.parent[b:b + 1], inp.n_nodes[b:b + 1], inp.tokens[b:b + 1]
+        oracle.tree_build(par, nn, inp.lens[b:b + 1])
+        o0, o1 = int(a.prefix_offsets[b]), int(a.prefix_offsets[b + 1])
+        oracle.tree_verify_attn(q[b:b + 1], kt[b:b + 1], vt[b:b + 1], kp[o0:o1], vp[o0:o1],
+                                np.array([0, o1 - o0]), par, nn)
+        oracle.tree_accept(par, tok, tgts[b], nn)
+        queries += int(nn[0]) * w.Hq
+        steps += 1
+    dt = time.perf_counter() - t0
+    return dict(value=queries / dt, unit=UNIT, cores=int(blas), kind="oracle",
+                sample=f"{steps} single-sequence passes of the full path (expand/rerank when the "
+                       f"tree is dynamic, tree build, float64 masked attention, accept) over "
+                       f"sequences 0..{min(steps, w.B) - 1}, {dt:.1f} s of CPU time")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path does "
+              f"not shard across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    inp = Inputs(w)
+    g = gpu_leg(args, inp)
+    parent, n_nodes = g["tree"]
+    queries = int(np.sum(n_nodes)) * w.Hq
+    value = queries / (g["step_ms"] * 1e-3)
+    abytes = inp.algorithmic_bytes(n_nodes)
+    aflops = inp.algorithmic_flops(parent, n_nodes)
+    achieved_gbs = abytes / (g["attn_ms"] * 1e-3) / 1e9
+    mfma_tflops = aflops / (g["attn_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": g["step_ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "prefix_tokens": int(inp.lens.sum()),
+                   "tree_nodes": int(np.sum(n_nodes)), "tree": "dynamic" if inp.dynamic else "static",
+                   "parallelism": "single GPU", "input_copies_rotated": g["copies"]},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(w.name),
+                     "kernel": ("tree_verify_attn (attn_bf16_partial + attn_combine)"
+                                if w.dtype == "bf16" else "tree_verify_attn (attn_f32)"),
+                     "bytes_per_launch": abytes, "launch_ms": g["attn_ms"],
+                     "mfma_tflops": mfma_tflops, "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "ms_per_step_wall": g["step_ms_wall"],
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_leg(args, inp, g["tree"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
