@@ -331,7 +331,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": recorded_traffic(w.name),
-                     "kernel": ("tree_verify_attn (attn_bf16_partial + attn_combine)"
+                     "kernel": ("tree_verify_attn (attn_bf16 + attn_combine when split)"
                                 if w.dtype == "bf16" else "tree_verify_attn (attn_f32)"),
                      "bytes_per_launch": abytes, "launch_ms": g["attn_ms"],
                      "mfma_tflops": mfma_tflops, "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},

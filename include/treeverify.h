@@ -152,9 +152,10 @@ tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int max_st
  * scale <= 0 selects 1/sqrt(D).  Supported: dt = TV_BF16 with D in {64, 128}
  * (fp32 accumulation, bf16 output, round to nearest even) and dt = TV_F32 with
  * D % 4 == 0 and D <= 256.  k_prefix / v_prefix may be NULL when max_prefix_len == 0.
- * ws: caller workspace of tree_verify_attn_workspace_size(...) bytes for the split-KV
- * partial results (may be NULL when that size is 0).  Device errors: TV_SEQ_BAD_N,
- * TV_SEQ_BAD_PREFIX in seq_status (nullable).
+ * ws: caller workspace of tree_verify_attn_workspace_size(...) bytes for the partial
+ * results of sequences whose prefix spans several key chunks (may be NULL when that
+ * size is 0; no initialisation needed).  Calls sharing a workspace must not overlap.
+ * Device errors: TV_SEQ_BAD_N, TV_SEQ_BAD_PREFIX in seq_status (nullable).
  */
 size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
                                        int max_prefix_len);
