@@ -51,6 +51,9 @@ def parse():
                     help="bounded CPU work for the oracle baseline (0 disables it)")
     ap.add_argument("--attn-reps", type=int, default=20,
                     help="replays of the back-to-back attention graph for the kernel timing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times "
+                         "(the known-size reference for HBM byte counters), then exit")
     return ap.parse_args()
 
 
@@ -249,6 +252,19 @@ def gpu_leg(args, inp):
                 tree=tree_host)
 
 
+def copy_reference(mib):
+    """Three plain copy kernels of `mib` MiB: each reads and writes exactly mib MiB of HBM
+    (an elementwise kernel, not the runtime's memcpy, so that counters see it)."""
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": mib << 20, "launches": 3}), flush=True)
+
+
 def cpu_leg(args, inp, tree):
     """The oracle as it stands, on the host cores, over a bounded number of steps."""
     import oracle
@@ -309,6 +325,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path does "
               f"not shard across GPUs in this build)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib > 0:
+        copy_reference(args.copy_mib)
+        return
     import synth
     w = synth.WORKLOADS[args.workload]
     inp = Inputs(w)

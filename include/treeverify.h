@@ -118,7 +118,7 @@ tv_status tree_build(int B, int n_max, const int32_t* parent, const int32_t* n_n
  *   score fp32 [B][n_max] (root 0), n_nodes int32 [B]; padding -1 / -1 / 0.
  * frontier_token int32 [B][k] (nullable) receives the tokens of the new frontier by
  * rank at every step, for the caller's next draft pass.
- * Limits: 1 <= k <= 16, k <= vocab, max_steps >= 1, k + (max_steps-1)*k*k <= 4096,
+ * Limits: 1 <= k <= 16, k <= vocab <= 1048576, max_steps >= 1, k + (max_steps-1)*k*k <= 4096,
  * 1 <= n_max <= 64, 0 <= final_m <= n_max.  root_token may be NULL unless final_m > 0.
  * Device errors: TV_SEQ_NONFINITE (sticky for later steps), TV_SEQ_BAD_N (m), and
  * TV_SEQ_BAD_STATE (step > 1 without the previous step on this workspace).

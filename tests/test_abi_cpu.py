@@ -72,6 +72,7 @@ def test_expand_validation(L):
     assert _expand(L, step=0) == SHAPE
     assert _expand(L, step=4) == SHAPE
     assert _expand(L, vocab=3) == SHAPE
+    assert _expand(L, vocab=(1 << 20) + 1) == SHAPE
     assert _expand(L, final_m=65) == SHAPE
     assert _expand(L, final_m=-1) == SHAPE
     assert _expand(L, n_max=65) == SHAPE

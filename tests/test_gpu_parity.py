@@ -129,6 +129,9 @@ SMALL_EXPAND = [  # (B, k, S, V, m, quantised)
     (3, 1, 4, 16, 64, True), (3, 2, 3, 16, 9, True), (4, 3, 3, 16, 64, True),
     (2, 5, 4, 100, 30, False), (5, 8, 3, 1000, 64, False), (2, 10, 4, 777, 40, True),
     (2, 16, 2, 4096, 64, False), (3, 4, 5, 33, 2, True), (2, 6, 6, 50, 1, False),
+    # rows split over many chunks: ties across lanes, waves and chunks; odd vocab sizes
+    (2, 10, 3, 50000, 40, True), (3, 4, 3, 20001, 16, True), (1, 16, 2, 9001, 64, False),
+    (1, 2, 2, 600000, 4, True), (1, 3, 2, 600001, 5, False),
 ]
 
 
@@ -146,12 +149,13 @@ def test_expand_small(case):
     _check_expand(levels, k, m, rng.integers(0, V, size=B))
 
 
-def test_expand_nonfinite_and_m_per_seq():
+@pytest.mark.parametrize("V", [64, 40000])
+def test_expand_nonfinite_and_m_per_seq(V):
     rng = np.random.default_rng(7)
-    B, k, S, V = 4, 3, 3, 64
+    B, k, S = 4, 3, 3
     levels = [(rng.standard_normal((B, 1 if s == 0 else k, V)) * 2).astype(np.float32) for s in range(S)]
-    levels[1][1, 2, 11] = np.nan
-    levels[2][2, 0, 0] = np.inf
+    levels[1][1, 2, 11 * V // 64] = np.nan
+    levels[2][2, 0, V - 1] = np.inf
     m_seq = np.array([5, 20, 64, 70], dtype=np.int32)          # the last is out of range
     _check_expand(levels, k, 64, rng.integers(0, V, size=B), m_per_seq=m_seq)
 

@@ -9,17 +9,19 @@
 // so the kept set is exactly reproducible.
 //
 // Two kernels per call:
-//   expand_rows_kernel   one workgroup per (sequence, frontier row): streams the
-//                        vocabulary once for max, finiteness and a per-thread top-k,
-//                        once more (L2-resident) for the float64 sum of exponentials,
-//                        and appends k children to the sequence's pool.
-//   expand_select_kernel one workgroup per sequence: ranks this level's children
-//                        into the next frontier; on the last level ranks the whole
-//                        pool, keeps the best m-1 and writes the tree in (depth,
-//                        creation) order with remapped parents.
-// Workspace per sequence: a header {status, pool count, next step}, the frontier
-// (pool slots by rank), one bad-row flag per frontier row, then the pool of
-// {parent slot, token, score, depth} records in creation order.
+//   expand_rows_kernel   grid (chunk, frontier row, sequence).  Each workgroup reads
+//                        one chunk of one logit row once (coalesced loads held in
+//                        registers) and records the chunk's maximum, its float64 sum of
+//                        exp(l - chunk max), a non-finite flag and its top-k.
+//   expand_select_kernel one workgroup per sequence.  One wave per frontier row merges
+//                        the chunk records into the row's log-sum-exp and top-k and
+//                        appends the k children to the pool; then this level's
+//                        children are ranked into the next frontier, and on the last
+//                        level the whole pool is ranked, the best m-1 kept and the tree
+//                        written in (depth, creation) order with remapped parents.
+// Workspace per sequence: a header {status, pool count, next step, frontier}, the pool
+// of {parent slot, token, score, depth} records in creation order, then one record
+// per (frontier row, chunk).
 #include <math.h>
 
 #include "tv_internal.h"
@@ -28,8 +30,15 @@ namespace tv {
 
 constexpr int kTopKMax = 16;
 constexpr int kPoolMax = 4096;
-constexpr int kRowThreads = 512;
+constexpr int kChunkThreads = 256;
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kMaxRowChunks = 64;        // chunks per logit row (one lane each when merging)
+constexpr int kMaxChunkElems = 64 * kChunkThreads;
+constexpr int kMaxVocab = kMaxRowChunks * kMaxChunkElems;
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+static_assert(kSelWaves >= kTopKMax, "one select wave per frontier row");
+static_assert(kChunkWaves * kTopKMax <= kWave, "the chunk's wave lists fit one wave");
 
 struct PoolEntry {
   int32_t parent_slot;  // pool slot of the parent, -1 for the root
@@ -44,14 +53,26 @@ struct SeqHeader {
   int32_t next_step;
   int32_t pad[13];
   int32_t frontier[kTopKMax];
-  int32_t row_bad[kTopKMax];
+};
+
+// What one workgroup of expand_rows_kernel learns about its chunk of a logit row.
+struct ChunkRec {
+  double sum;                // sum over the chunk of exp(l - max), float64
+  float max;                 // chunk maximum
+  int32_t bad;               // a NaN or infinite logit was seen
+  float val[kTopKMax];       // chunk top-k, best first; -inf / INT32_MAX past its end
+  int32_t id[kTopKMax];
 };
 
 __host__ __device__ inline int64_t pool_capacity(int k, int max_steps) {
   return (int64_t)k + (int64_t)(max_steps - 1) * k * k;
 }
-__host__ __device__ inline size_t seq_stride_bytes(int k, int max_steps) {
+__host__ __device__ inline size_t chunk_rec_offset(int k, int max_steps) {
   size_t s = sizeof(SeqHeader) + (size_t)pool_capacity(k, max_steps) * sizeof(PoolEntry);
+  return (s + 255) & ~(size_t)255;
+}
+__host__ __device__ inline size_t seq_stride_bytes(int k, int max_steps) {
+  size_t s = chunk_rec_offset(k, max_steps) + (size_t)k * kMaxRowChunks * sizeof(ChunkRec);
   return (s + 255) & ~(size_t)255;
 }
 // pool slots used before level `step` (1-based): k after level 1, k*k per level after
@@ -59,215 +80,225 @@ __host__ __device__ inline int pool_base(int k, int step) {
   return step == 1 ? 0 : k + (step - 2) * k * k;
 }
 
-__device__ __forceinline__ uint32_t ordered(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0 so equal values compare equal
+// ---- wave-wide reductions (every lane active; every lane gets the result)
+
+// Order-preserving map of a float to an unsigned key: a larger value has a larger key,
+// -0 and +0 share one key, and every finite value or -inf maps above 0, which is kept
+// to mean "no candidate".
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-// a (value, id) pair as one integer: larger value first, then lower id
-__device__ __forceinline__ uint64_t rank_key(float v, int id) {
-  return ((uint64_t)ordered(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // 0 is the identity of unsigned max, so the compiler folds this into v_max_u32_dpp
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror: max over 8 lanes
+  v = max(v, dpp_u32<0x140>(v));   // row_mirror: max over the 16-lane row
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  const uint32_t k = wave_max_u32(fkey(v));
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// Insert (v, id) into a list sorted best first; ids arrive in increasing order.
-__device__ __forceinline__ void topk_insert(float (&val)[kTopKMax], int (&idx)[kTopKMax], int k,
-                                            float v, int id) {
-  if (!(v > val[k - 1])) return;
-  float cv = v;
-  int ci = id;
+// One selection round over the wave: the lane whose candidate ranks first by (value
+// descending, id ascending), given each lane's fkey (0 = no candidate) and id.
+// Returns -1 when no lane has a candidate.
+__device__ __forceinline__ int wave_argbest(uint32_t key, int id) {
+  const uint32_t m = wave_max_u32(key);
+  if (m == 0u) return -1;
+  const uint64_t ball = __ballot(key == m);
+  if (__popcll(ball) == 1) return __ffsll((unsigned long long)ball) - 1;
+  const int mid = wave_min_i32(key == m ? id : INT32_MAX);         // equal values: lower id
+  return __ffsll((unsigned long long)__ballot(key == m && id == mid)) - 1;
+}
+
+// The best two of this lane's elements x[j] by (value desc, j asc) among those ranked
+// after (after_v, after_j); j = EPT marks an empty place.  -inf elements (past the chunk)
+// are never taken.
+template <int EPT>
+__device__ __forceinline__ void best_two(const float (&x)[EPT], float after_v, int after_j,
+                                         float& v1, int& j1, float& v2, int& j2) {
+  v1 = v2 = -INFINITY;
+  j1 = j2 = EPT;
 #pragma unroll
-  for (int j = 0; j < kTopKMax; ++j) {
-    if (j < k) {
-      const bool beats = cv > val[j] || (cv == val[j] && ci < idx[j]);
-      if (beats) {
-        const float tv = val[j];
-        const int ti = idx[j];
-        val[j] = cv;
-        idx[j] = ci;
-        cv = tv;
-        ci = ti;
-      }
-    }
+  for (int j = 0; j < EPT; ++j) {
+    const float v = x[j];
+    const bool after = v < after_v || (v == after_v && j > after_j);
+    const bool c1 = after && v > v1;
+    const bool c2 = after && v > v2;
+    v2 = c1 ? v1 : (c2 ? v : v2);
+    j2 = c1 ? j1 : (c2 ? j : j2);
+    v1 = c1 ? v : v1;
+    j1 = c1 ? j : j1;
   }
 }
 
-// k rounds of a wave-wide maximum over each lane's list head; the winner pops its head.
-// Result (valid in every lane): out_v/out_i[0..k) best first.
-__device__ __forceinline__ void wave_merge_topk(float (&val)[kTopKMax], int (&idx)[kTopKMax], int k,
-                                                float* out_v, int* out_i, bool write) {
-  for (int t = 0; t < k; ++t) {
-    const uint64_t mine = idx[0] == INT32_MAX ? 0ull : rank_key(val[0], idx[0]);
-    const uint64_t best = wave_max_u64(mine);
-    if (best != 0ull && mine == best) {
-#pragma unroll
-      for (int j = 0; j < kTopKMax - 1; ++j) {
-        val[j] = val[j + 1];
-        idx[j] = idx[j + 1];
-      }
-      val[kTopKMax - 1] = -INFINITY;
-      idx[kTopKMax - 1] = INT32_MAX;
-    }
-    if (write && lane_id() == 0) {
-      if (best == 0ull) {
-        out_v[t] = -INFINITY;
-        out_i[t] = INT32_MAX;
-      } else {
-        const uint32_t o = (uint32_t)(best >> 32);
-        const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-        out_v[t] = __uint_as_float(u);
-        out_i[t] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(kRowThreads) void expand_rows_kernel(
-    char* __restrict__ ws, size_t stride, int k, int step, int rows, int vocab,
-    const float* __restrict__ logits) {
-  const int r = blockIdx.x;
-  const int b = blockIdx.y;
-  SeqHeader* hdr = (SeqHeader*)(ws + (size_t)b * stride);
-  PoolEntry* pool = (PoolEntry*)(ws + (size_t)b * stride + sizeof(SeqHeader));
+template <int EPT, bool VEC>
+__global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
+    char* __restrict__ ws, size_t stride, size_t rec_off, int k, int step, int rows, int vocab,
+    int chunk, const float* __restrict__ logits) {
+  const int c = blockIdx.x;
+  const int r = blockIdx.y;
+  const int b = blockIdx.z;
+  char* seq = ws + (size_t)b * stride;
+  const SeqHeader* hdr = (const SeqHeader*)seq;
   if (step > 1 && (hdr->status != TV_SEQ_OK || hdr->next_step != step)) return;
+  ChunkRec* rec = (ChunkRec*)(seq + rec_off) + (size_t)r * kMaxRowChunks + c;
 
-  __shared__ float s_wv[kRowThreads / kWave][kTopKMax];
-  __shared__ int s_wi[kRowThreads / kWave][kTopKMax];
-  __shared__ float s_max[kRowThreads / kWave];
-  __shared__ double s_sum[kRowThreads / kWave];
-  __shared__ int s_bad[kRowThreads / kWave];
-  __shared__ float s_topv[kTopKMax];
-  __shared__ int s_topi[kTopKMax];
+  __shared__ float s_wv[kChunkWaves][kTopKMax];
+  __shared__ int s_wi[kChunkWaves][kTopKMax];
+  __shared__ float s_max[kChunkWaves];
+  __shared__ int s_bad[kChunkWaves];
+  __shared__ double s_sum[kChunkWaves];
 
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const float* row = logits + ((size_t)b * rows + r) * (size_t)vocab;
+  const int e0 = c * chunk;
+  const int e1 = min(vocab, e0 + chunk);
+  // element j of this thread; ids increase with j
+  auto id_of = [&](int j) {
+    return VEC ? e0 + 4 * (tid + kChunkThreads * (j >> 2)) + (j & 3) : e0 + tid + kChunkThreads * j;
+  };
 
-  float val[kTopKMax];
-  int idx[kTopKMax];
+  // every load is issued before any is used (addresses clamped into the chunk, values
+  // past its end replaced by -inf afterwards), so they are all in flight together
+  float x[EPT];
+  if constexpr (VEC) {
 #pragma unroll
-  for (int j = 0; j < kTopKMax; ++j) {
-    val[j] = -INFINITY;
-    idx[j] = INT32_MAX;
-  }
-  float mx = -INFINITY;
-  bool bad = false;
-
-  const bool vec = (vocab % 4 == 0) && ((((uintptr_t)row) & 15) == 0);
-  if (vec) {
-    const float4* row4 = (const float4*)row;
-    const int n4 = vocab / 4;
-    for (int q = tid; q < n4; q += kRowThreads) {
-      const float4 x = row4[q];
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = xs[e];
-        bad |= !isfinite(v);
-        mx = fmaxf(mx, v);
-        topk_insert(val, idx, k, v, 4 * q + e);
-      }
+    for (int q = 0; q < EPT / 4; ++q) {
+      const int i0 = min(id_of(4 * q), e1 - 4);           // chunk and vocab are 4-aligned
+      const float4 v = *(const float4*)(row + i0);
+      x[4 * q] = v.x;
+      x[4 * q + 1] = v.y;
+      x[4 * q + 2] = v.z;
+      x[4 * q + 3] = v.w;
     }
   } else {
-    for (int v = tid; v < vocab; v += kRowThreads) {
-      const float x = row[v];
-      bad |= !isfinite(x);
-      mx = fmaxf(mx, x);
-      topk_insert(val, idx, k, x, v);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) x[j] = row[min(id_of(j), e1 - 1)];
+  }
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const bool in = id_of(j) < e1;
+    bad |= in && !isfinite(x[j]);
+    x[j] = in ? x[j] : -INFINITY;
+  }
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) mx = fmaxf(mx, x[j]);
+  float h1v, h2v;
+  int h1j, h2j;
+  best_two(x, INFINITY, -1, h1v, h1j, h2v, h2j);
+
+  // this wave's top-k: k rounds over the lanes' heads.  A lane keeps its best two; when
+  // it wins with its second already promoted, it rescans for the two after the winner.
+  bool second_known = true;
+  for (int t = 0; t < k; ++t) {
+    const int win = wave_argbest(h1j < EPT ? fkey(h1v) : 0u, id_of(h1j));
+    if (win < 0) {
+      if (lane == 0) {
+        s_wv[wave][t] = -INFINITY;
+        s_wi[wave][t] = INT32_MAX;
+      }
+      continue;
+    }
+    if (lane == win) {
+      s_wv[wave][t] = h1v;
+      s_wi[wave][t] = id_of(h1j);
+      if (second_known) {
+        h1v = h2v;
+        h1j = h2j;
+        second_known = false;
+      } else {
+        float a1v, a2v;
+        int a1j, a2j;
+        best_two(x, h1v, h1j, a1v, a1j, a2v, a2j);
+        h1v = a1v;
+        h1j = a1j;
+        h2v = a2v;
+        h2j = a2j;
+        second_known = true;
+      }
     }
   }
 
-  // block max and finiteness
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float wm = wave_max_f32(mx);
   const bool wbad = __ballot(bad) != 0ull;
-  if (lane_id() == 0) {
-    s_max[wave] = mx;
+  if (lane == 0) {
+    s_max[wave] = wm;
     s_bad[wave] = wbad;
   }
-  wave_merge_topk(val, idx, k, s_wv[wave], s_wi[wave], lane_id() == 0);
   __syncthreads();
   float M = s_max[0];
   int anybad = s_bad[0];
-  for (int w = 1; w < kRowThreads / kWave; ++w) {
+#pragma unroll
+  for (int w = 1; w < kChunkWaves; ++w) {
     M = fmaxf(M, s_max[w]);
     anybad |= s_bad[w];
   }
   if (anybad) {
-    if (tid == 0) hdr->row_bad[r] = 1;
+    if (tid == 0) rec->bad = 1;
     return;
   }
 
-  // second pass: float64 sum of exp(l - max); the row is still in L2
-  double sum = 0.0;
+  // float64 sum of exp(l - chunk max); elements past the chunk are -inf and add 0
   const double Md = (double)M;
-  if (vec) {
-    const float4* row4 = (const float4*)row;
-    const int n4 = vocab / 4;
-    for (int q = tid; q < n4; q += kRowThreads) {
-      const float4 x = row4[q];
-      sum += exp((double)x.x - Md) + exp((double)x.y - Md) + exp((double)x.z - Md) +
-             exp((double)x.w - Md);
-    }
-  } else {
-    for (int v = tid; v < vocab; v += kRowThreads) sum += exp((double)row[v] - Md);
-  }
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if (lane_id() == 0) s_sum[wave] = sum;
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) sum += exp((double)x[j] - Md);
+  sum = wave_sum_f64(sum);
+  if (lane == 0) s_sum[wave] = sum;
+  __syncthreads();
 
-  // merge the per-wave lists (wave 0; lane l takes candidates l and l+64)
   if (wave == 0) {
-    const int nc = (kRowThreads / kWave) * k;
-    float v2[kTopKMax];
-    int i2[kTopKMax];
-#pragma unroll
-    for (int j = 0; j < kTopKMax; ++j) {
-      v2[j] = -INFINITY;
-      i2[j] = INT32_MAX;
-    }
-    for (int c = lane_id(); c < nc; c += kWave) {
-      const float cv = s_wv[c / k][c % k];
-      const int ci = s_wi[c / k][c % k];
-      if (ci == INT32_MAX) continue;
-      // small insertion by full comparison (candidate ids are not ordered here)
-      float pv = cv;
-      int pi = ci;
-#pragma unroll
-      for (int j = 0; j < kTopKMax; ++j) {
-        if (j < k) {
-          const bool beats = pv > v2[j] || (pv == v2[j] && pi < i2[j]);
-          if (beats) {
-            const float tv = v2[j];
-            const int ti = i2[j];
-            v2[j] = pv;
-            i2[j] = pi;
-            pv = tv;
-            pi = ti;
-          }
+    // the chunk's top-k from the wave lists: lane l holds candidate l % k of wave l / k
+    const int nc = kChunkWaves * k;
+    float cv = lane < nc ? s_wv[lane / k][lane % k] : -INFINITY;
+    int ci = lane < nc ? s_wi[lane / k][lane % k] : INT32_MAX;
+    for (int t = 0; t < k; ++t) {
+      const int win = wave_argbest(ci != INT32_MAX ? fkey(cv) : 0u, ci);
+      if (win < 0) {
+        if (lane == 0) {
+          rec->val[t] = -INFINITY;
+          rec->id[t] = INT32_MAX;
         }
+        continue;
+      }
+      if (lane == win) {
+        rec->val[t] = cv;
+        rec->id[t] = ci;
+        cv = -INFINITY;
+        ci = INT32_MAX;
       }
     }
-    wave_merge_topk(v2, i2, k, s_topv, s_topi, lane_id() == 0);
-  }
-  __syncthreads();
-  if (tid < k) {
-    double S = 0.0;
-    for (int w = 0; w < kRowThreads / kWave; ++w) S += s_sum[w];
-    const float lse32 = (float)(Md + log(S));
-    int pslot = -1;
-    float pscore = 0.f;
-    int pdepth = 0;
-    if (step > 1) {
-      pslot = hdr->frontier[r];
-      pslot = pslot < 0 ? 0 : (pslot >= pool_base(k, step) ? pool_base(k, step) - 1 : pslot);
-      pscore = pool[pslot].score;
-      pdepth = pool[pslot].depth;
+    if (lane == 0) {
+      double S = 0.0;
+      for (int w = 0; w < kChunkWaves; ++w) S += s_sum[w];
+      rec->sum = S;
+      rec->max = M;
+      rec->bad = 0;
     }
-    const float logp = __fsub_rn(s_topv[tid], lse32);
-    PoolEntry e;
-    e.parent_slot = pslot;
-    e.token = s_topi[tid];
-    e.score = __fadd_rn(pscore, logp);
-    e.depth = pdepth + 1;
-    pool[pool_base(k, step) + r * k + tid] = e;
-    if (tid == 0) hdr->row_bad[r] = 0;
   }
 }
 
@@ -276,61 +307,137 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
-    char* __restrict__ ws, size_t stride, int k, int step, int rows, int final_m,
-    const int32_t* __restrict__ m_per_seq, const int32_t* __restrict__ root_token, int n_max,
-    int32_t* __restrict__ parent, int32_t* __restrict__ token, float* __restrict__ score,
-    int32_t* __restrict__ n_nodes, int32_t* __restrict__ frontier_token,
+    char* __restrict__ ws, size_t stride, size_t rec_off, int k, int step, int rows, int nch,
+    int final_m, const int32_t* __restrict__ m_per_seq, const int32_t* __restrict__ root_token,
+    int n_max, int32_t* __restrict__ parent, int32_t* __restrict__ token,
+    float* __restrict__ score, int32_t* __restrict__ n_nodes, int32_t* __restrict__ frontier_token,
     int32_t* __restrict__ seq_status) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  SeqHeader* hdr = (SeqHeader*)(ws + (size_t)b * stride);
-  PoolEntry* pool = (PoolEntry*)(ws + (size_t)b * stride + sizeof(SeqHeader));
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  char* seq = ws + (size_t)b * stride;
+  SeqHeader* hdr = (SeqHeader*)seq;
+  PoolEntry* pool = (PoolEntry*)(seq + sizeof(SeqHeader));
+  const ChunkRec* recs = (const ChunkRec*)(seq + rec_off);
 
-  __shared__ float s_score[kPoolMax];
+  __shared__ __attribute__((aligned(16))) float s_score[kPoolMax + 16];
   __shared__ short s_pos[kPoolMax];
+  __shared__ int s_tok[kTopKMax * kTopKMax];
   __shared__ int s_front[kTopKMax];
   __shared__ int s_kept[TV_MAX_NODES];
+  __shared__ int s_kdep[TV_MAX_NODES];
   __shared__ int s_nkept;
   __shared__ int s_status;
+  __shared__ int s_m;
+  __shared__ int s_rowbad;
 
   const int base = pool_base(k, step);
   const int added = rows * k;
   const int count = base + added;
+
+  // ---- every independent global read first: the header and m (thread 0), and per
+  // frontier row (wave rr, lane c = chunk c) the chunk records and the parent node
   if (tid == 0) {
     int st = TV_SEQ_OK;
     if (step > 1) {
       st = hdr->status;
       if (st == TV_SEQ_OK && (hdr->next_step != step || hdr->count != base)) st = TV_SEQ_BAD_STATE;
     }
-    if (st == TV_SEQ_OK) {
-      for (int rr = 0; rr < rows; ++rr)
-        if (hdr->row_bad[rr]) st = TV_SEQ_NONFINITE;
-    }
-    if (st == TV_SEQ_OK && final_m > 0) {
-      const int m = m_per_seq ? m_per_seq[b] : final_m;
-      if (m < 1 || m > n_max) st = TV_SEQ_BAD_N;
-    }
     s_status = st;
+    s_m = final_m > 0 ? (m_per_seq ? m_per_seq[b] : final_m) : 0;
     s_nkept = 0;
+    s_rowbad = 0;
   }
   if (tid < kTopKMax) s_front[tid] = -1;
+  const int rr = wave;
+  const bool merger = rr < rows;
+  const bool has = merger && lane < nch;
+  const ChunkRec* rec = recs + (size_t)rr * kMaxRowChunks + lane;
+  float hv[kTopKMax];
+  int hi[kTopKMax];
+  float cmax = -INFINITY;
+  double csum = 0.0;
+  int cbad = 0;
+  int pslot = -1;
+  float pscore = 0.f;
+  int pdepth = 0;
+  if (merger) {
+    // records of a sequence that is not ok are stale but never used
+    if (has) {
+      cbad = rec->bad;
+      cmax = rec->max;
+      csum = rec->sum;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) {
+      hv[j] = has && j < k ? rec->val[j] : -INFINITY;
+      hi[j] = has && j < k ? rec->id[j] : INT32_MAX;
+    }
+    if (step > 1) {
+      pslot = hdr->frontier[rr];
+      pslot = pslot < 0 ? 0 : (pslot >= base ? base - 1 : pslot);
+      pscore = pool[pslot].score;
+      pdepth = pool[pslot].depth;
+    }
+  }
+  __syncthreads();
+
+  // ---- wave rr merges the chunk records of frontier row rr: lse = M + log(sum over
+  // chunks of sum_c * exp(max_c - M)) in float64, rounded once to float32; the row's
+  // top-k by a k-way merge of the sorted chunk lists
+  if (s_status == TV_SEQ_OK && merger) {
+    if (__ballot(has && cbad != 0) != 0ull) {
+      if (lane == 0) s_rowbad = 1;
+    } else {
+      const float M = wave_max_f32(cmax);
+      const double S = wave_sum_f64(has ? csum * exp((double)cmax - (double)M) : 0.0);
+      const float lse32 = (float)((double)M + log(S));
+      for (int t = 0; t < k; ++t) {
+        // the chunks together hold at least k finite candidates (vocab >= k)
+        const int win = wave_argbest(hi[0] != INT32_MAX ? fkey(hv[0]) : 0u, hi[0]);
+        if (lane == win) {
+          PoolEntry e;
+          e.parent_slot = pslot;
+          e.token = hi[0];
+          e.score = __fadd_rn(pscore, __fsub_rn(hv[0], lse32));
+          e.depth = pdepth + 1;
+          pool[base + rr * k + t] = e;
+          s_score[rr * k + t] = e.score;
+          s_tok[rr * k + t] = e.token;
+#pragma unroll
+          for (int j = 0; j < kTopKMax - 1; ++j) {
+            hv[j] = hv[j + 1];
+            hi[j] = hi[j + 1];
+          }
+          hv[kTopKMax - 1] = -INFINITY;
+          hi[kTopKMax - 1] = INT32_MAX;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int st = s_status;
+    if (st == TV_SEQ_OK && s_rowbad) st = TV_SEQ_NONFINITE;
+    if (st == TV_SEQ_OK && final_m > 0 && (s_m < 1 || s_m > n_max)) st = TV_SEQ_BAD_N;
+    s_status = st;
+  }
   __syncthreads();
   const int st = s_status;
 
   if (st == TV_SEQ_OK) {
-    for (int c = tid; c < added; c += kSelThreads) s_score[c] = pool[base + c].score;
-    __syncthreads();
     // next frontier: the k best children of this level by (score desc, creation asc)
     for (int c = tid; c < added; c += kSelThreads) {
       const float sc = s_score[c];
       int rank = 0;
       for (int o = 0; o < added; ++o) rank += better(s_score[o], o, sc, c);
-      if (rank < k) s_front[rank] = base + c;
+      if (rank < k) s_front[rank] = c;
     }
     __syncthreads();
     if (tid < k) {
-      hdr->frontier[tid] = s_front[tid];
-      if (frontier_token) frontier_token[(size_t)b * k + tid] = pool[s_front[tid]].token;
+      hdr->frontier[tid] = base + s_front[tid];
+      if (frontier_token) frontier_token[(size_t)b * k + tid] = s_tok[s_front[tid]];
     }
   } else if (frontier_token && tid < k) {
     frontier_token[(size_t)b * k + tid] = -1;
@@ -340,28 +447,36 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     __syncthreads();
     int keep = 0;
     if (st == TV_SEQ_OK) {
-      const int m = m_per_seq ? m_per_seq[b] : final_m;
-      keep = min(m - 1, count);
-      for (int c = tid; c < count; c += kSelThreads) {
-        s_score[c] = pool[c].score;
-        s_pos[c] = -1;
+      keep = min(s_m - 1, count);
+      // scores padded to a multiple of 16 with -inf, which never ranks above a score
+      const int count16 = (count + 15) & ~15;
+      for (int c = tid; c < count16; c += kSelThreads) {
+        s_score[c] = c < count ? pool[c].score : -INFINITY;
+        if (c < count) s_pos[c] = -1;
       }
       __syncthreads();
       for (int c = tid; c < count; c += kSelThreads) {
         const float sc = s_score[c];
         int rank = 0;
-        for (int o = 0; o < count && rank < keep; ++o) rank += better(s_score[o], o, sc, c);
+        for (int o = 0; o < count16 && rank < keep; o += 16) {
+          const f32x4* q4 = (const f32x4*)(s_score + o);
+          const f32x4 w[4] = {q4[0], q4[1], q4[2], q4[3]};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) rank += better(w[j >> 2][j & 3], o + j, sc, c);
+        }
         if (rank < keep) s_kept[atomicAdd(&s_nkept, 1)] = c;
       }
+      __syncthreads();
+      if (tid < keep) s_kdep[tid] = pool[s_kept[tid]].depth;
       __syncthreads();
       // output position: root first, then by (depth, creation)
       if (tid < keep) {
         const int me = s_kept[tid];
-        const int dme = pool[me].depth;
+        const int dme = s_kdep[tid];
         int before = 0;
         for (int o = 0; o < keep; ++o) {
           const int other = s_kept[o];
-          const int dot = pool[other].depth;
+          const int dot = s_kdep[o];
           before += (dot < dme) || (dot == dme && other < me);
         }
         s_pos[me] = (short)(1 + before);
@@ -401,6 +516,41 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   }
 }
 
+// Chunking of a logit row: about 1024 workgroups in all, each chunk between 1024 and
+// 8192 logits where the vocabulary allows, at most kMaxRowChunks chunks per row.
+struct RowPlan {
+  int nch, chunk, ept;
+};
+static RowPlan row_plan(int B, int rows, int vocab) {
+  const long units = (long)B * rows;
+  const long want = (1024 + units - 1) / units;
+  const long lo = (vocab + 8191) / 8192;
+  const long hi = (vocab + 1023) / 1024;
+  long n = want < hi ? want : hi;
+  if (n < lo) n = lo;
+  if (n > kMaxRowChunks) n = kMaxRowChunks;
+  if (n < 1) n = 1;
+  int ch = (int)((vocab + n - 1) / n);
+  ch = (ch + 3) & ~3;
+  RowPlan p;
+  p.chunk = ch;
+  p.nch = (vocab + ch - 1) / ch;
+  p.ept = ch <= 8 * kChunkThreads ? 8 : ch <= 16 * kChunkThreads ? 16 : ch <= 32 * kChunkThreads ? 32 : 64;
+  return p;
+}
+
+template <int EPT>
+static void launch_rows(bool vec, dim3 grid, hipStream_t stream, char* ws, size_t stride,
+                        size_t rec_off, int k, int step, int rows, int vocab, int chunk,
+                        const float* logits) {
+  if (vec)
+    hipLaunchKernelGGL((expand_rows_kernel<EPT, true>), grid, dim3(kChunkThreads), 0, stream, ws,
+                       stride, rec_off, k, step, rows, vocab, chunk, logits);
+  else
+    hipLaunchKernelGGL((expand_rows_kernel<EPT, false>), grid, dim3(kChunkThreads), 0, stream, ws,
+                       stride, rec_off, k, step, rows, vocab, chunk, logits);
+}
+
 }  // namespace tv
 
 TV_API size_t tree_expand_workspace_size(int B, int k, int max_steps) {
@@ -417,20 +567,30 @@ TV_API tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int
                                     hipStream_t stream) {
   if (!logits) return TV_ERR_NULL;
   if (B < 1 || k < 1 || k > tv::kTopKMax || max_steps < 1 || step < 1 || step > max_steps ||
-      vocab < k || n_max < 1 || n_max > TV_MAX_NODES || final_m < 0 || final_m > n_max)
+      vocab < k || vocab > tv::kMaxVocab || n_max < 1 || n_max > TV_MAX_NODES || final_m < 0 || final_m > n_max)
     return TV_ERR_SHAPE;
   if (tv::pool_capacity(k, max_steps) > tv::kPoolMax) return TV_ERR_SHAPE;
   if (final_m > 0 && (!parent || !token || !score || !n_nodes || !root_token)) return TV_ERR_NULL;
   const size_t need = tree_expand_workspace_size(B, k, max_steps);
   if (!ws || ws_bytes < need) return TV_ERR_WORKSPACE;
   const size_t stride = tv::seq_stride_bytes(k, max_steps);
+  const size_t rec_off = tv::chunk_rec_offset(k, max_steps);
   const int rows = step == 1 ? 1 : k;
-  hipLaunchKernelGGL(tv::expand_rows_kernel, dim3(rows, B), dim3(tv::kRowThreads), 0, stream,
-                     (char*)ws, stride, k, step, rows, vocab, logits);
+  const tv::RowPlan rp = tv::row_plan(B, rows, vocab);
+  const bool vec = vocab % 4 == 0 && ((uintptr_t)logits & 15) == 0;
+  const dim3 grid(rp.nch, rows, B);
+  if (rp.ept == 8)
+    tv::launch_rows<8>(vec, grid, stream, (char*)ws, stride, rec_off, k, step, rows, vocab, rp.chunk, logits);
+  else if (rp.ept == 16)
+    tv::launch_rows<16>(vec, grid, stream, (char*)ws, stride, rec_off, k, step, rows, vocab, rp.chunk, logits);
+  else if (rp.ept == 32)
+    tv::launch_rows<32>(vec, grid, stream, (char*)ws, stride, rec_off, k, step, rows, vocab, rp.chunk, logits);
+  else
+    tv::launch_rows<64>(vec, grid, stream, (char*)ws, stride, rec_off, k, step, rows, vocab, rp.chunk, logits);
   tv_status s = tv::launch_status();
   if (s != TV_OK) return s;
   hipLaunchKernelGGL(tv::expand_select_kernel, dim3(B), dim3(tv::kSelThreads), 0, stream,
-                     (char*)ws, stride, k, step, rows, final_m, m_per_seq, root_token, n_max,
-                     parent, token, score, n_nodes, frontier_token, seq_status);
+                     (char*)ws, stride, rec_off, k, step, rows, rp.nch, final_m, m_per_seq,
+                     root_token, n_max, parent, token, score, n_nodes, frontier_token, seq_status);
   return tv::launch_status();
 }
