@@ -245,6 +245,23 @@ def test_attn_one_hot_mask_exact(G, L):
     assert np.all(o[1, int(nn[1]):] == 0.0)
 
 
+@pytest.mark.parametrize("G,n_max", [(8, 64), (4, 30), (1, 64), (1, 20)])
+def test_attn_score_outliers(G, n_max):
+    """Keys whose scores lie far above every earlier key of their chunk: beyond the
+    range a fixed per-chunk softmax reference can carry, so the rows involved must be
+    recomputed exactly (here the weights are nearly one-hot on the outliers)."""
+    Hkv = 2
+    inp, parent, nn = synth.random_attention_case(77 + G, 2, G * Hkv, Hkv, 128, (5000, 700),
+                                                  (n_max, n_max - 3), std=0.5, n_max=n_max)
+    u = synth.bf16_bits(np.full(128, 0.7, np.float32))
+    big = synth.bf16_bits(np.full(128, 5.6, np.float32))       # score 8x that of u.u
+    inp.q[:] = u
+    inp.k_prefix[4321, 1] = big                                # a late prefix key, head 1
+    inp.k_prefix[5000 + 650, 0] = big                          # sequence 1, head 0
+    inp.k_tree[0, n_max - 1, 0] = big                          # the deepest tree slot
+    _check_attn(inp, parent, nn, f"outliers G={G} n_max={n_max}")
+
+
 def test_attn_deterministic():
     inp, parent, nn = synth.random_attention_case(5, 3, 32, 8, 128, (3000, 100, 4097), (64, 20, 50))
     d = attn_device_inputs(inp)

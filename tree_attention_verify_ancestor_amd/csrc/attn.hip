@@ -60,12 +60,12 @@ struct AttnArgs {
 };
 
 struct AttnPlan {
-  int wq, wk, rows_per_wg, n_rb, chunk_keys, n_chunks, units, total_wgs, grid;
+  int wq, wk, qt, rows_per_wg, n_rb, chunk_keys, n_chunks, units, total_wgs, grid;
   size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
-constexpr int kWaves = 8;
-constexpr int kMaxChunks = 16;                       // key chunks per work unit (merge width)
+constexpr int kWaves = 4;
+constexpr int kMaxChunks = 32;                       // key chunks per work unit (merge width)
 constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kLdsBudget = 128 * 1024;
 
@@ -75,14 +75,17 @@ __host__ __device__ constexpr int n_buffers(int D, int wk) {
   return kLdsBudget / stage_bytes(D, wk) < 4 ? kLdsBudget / stage_bytes(D, wk) : 4;
 }
 
+// Work split of one workgroup (4 waves): WQ query groups x WK key splits, each wave
+// owning QT tiles of 32 rows (rows = node * G + head within the group).
 static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_prefix) {
   AttnPlan p{};
   const int G = Hq / Hkv;
   const int R = n_max * G;
-  if (R <= 64) { p.wq = 2; p.wk = 4; }
-  else if (R <= 128) { p.wq = 4; p.wk = 2; }
-  else { p.wq = 8; p.wk = 1; }
-  p.rows_per_wg = 32 * p.wq;
+  if (R <= 32) { p.wq = 1; p.wk = 4; p.qt = 1; }
+  else if (R <= 64) { p.wq = 1; p.wk = 4; p.qt = 2; }
+  else if (R <= 128) { p.wq = 2; p.wk = 2; p.qt = 2; }
+  else { p.wq = 4; p.wk = 1; p.qt = 2; }
+  p.rows_per_wg = 32 * p.qt * p.wq;
   p.n_rb = (R + p.rows_per_wg - 1) / p.rows_per_wg;
   const int kt = stage_keys(p.wk);
   p.units = B * Hkv * p.n_rb;
@@ -134,15 +137,35 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gsrc), "s"(lds_base) : "m0");
 }
+// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "m0");
+}
+
+// Maximum of a value over the two lanes l and l ^ 32 (which hold the two key halves of
+// one query row), in every lane.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 enum StageMode { kFull = 0, kMasked = 1 };
 
-template <int D, int WQ, int WK>
+template <int D, int WQ, int WK, int QT>
 __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
   constexpr int W = WQ * WK;
-  static_assert(W == kWaves, "eight waves per workgroup");
-  constexpr int NS = stage_keys(WK) / 32;       // 32-key subtiles per stage
+  static_assert(W == kWaves, "four waves per workgroup");
   constexpr int KT = stage_keys(WK);            // keys per stage
+  constexpr int NS = KT / 32;                   // 32-key subtiles per stage
+  constexpr int NSW = NS / WK;                  // subtiles per wave and stage
   constexpr int ROWB = 2 * D;                   // LDS bytes per K/V row (bf16, swizzled)
   constexpr int TILEB = KT * ROWB;              // K (or V) bytes per stage
   constexpr int STAGEB = 2 * TILEB;
@@ -152,10 +175,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
   constexpr int KBLKS = TILEB / 1024;
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
+  // Two row tiles per wave allow the software pipeline that overlaps one tile's
+  // softmax (vector ALUs) with the other tile's matrix products.
+  constexpr bool PIPE = QT == 2 && NBUF >= 3;
+  constexpr int LAG = PIPE ? 2 : 1;            // stages between a buffer's use and its refill
   static_assert(DMA * kAttnThreads * 16 == STAGEB, "stage must split into 1 KB DMA blocks");
   static_assert(NBUF >= 2 && NBUF <= 4, "two to four stage buffers");
+  static_assert(NSW * WK == NS && NSW >= 1, "whole subtiles per wave");
+  static_assert(QT == 1 || QT == 2, "one or two row tiles per wave");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGEB];
+  // LDS: the stage ring, reused at the end for the rows of all waves (fp32, padded)
+  constexpr int OSTR = D + 4;
+  constexpr int OB_FLOATS = W * QT * 32 * OSTR;
+  constexpr int OUT_BYTES = OB_FLOATS * 4 + W * QT * 32 * 8;
+  constexpr int SMEM = NBUF * STAGEB > OUT_BYTES ? NBUF * STAGEB : OUT_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   // ---- work item.  The order puts KV heads fastest, then row blocks, then chunks:
   // workgroups running together read the same token range of every head, i.e. whole
@@ -173,7 +207,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave / WK;
   const int wk = wave % WK;
   const int g = lane >> 5;
@@ -194,34 +228,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
 
   if (active) {
     const int has_tree = chunk == 0 ? 1 : 0;
+    const int n_full = c1 > c0 ? (c1 - c0) / KT : 0;           // prefix stages without a mask
     const int nst = (c1 > c0 ? (c1 - c0 + KT - 1) / KT : 0) + has_tree;
 
-    // queries of this wave: Q^T operands and the node's ancestor bitset.  A wave whose
-    // 32 rows all lie beyond the tree's rows still queues its DMA share and joins
-    // every barrier, but computes nothing.
-    const bool wave_live = row0 + wq * 32 < R;
-    const int rho = row0 + wq * 32 + ql;
-    const int rc = rho < R ? rho : R - 1;
-    const int qnode = rc / G;
-    const int qhead = kvh * G + rc % G;
-    bf16x8 qop[DS];
-    {
-      const __bf16* qp = a.q + (((size_t)b * a.n_max + qnode) * a.Hq + qhead) * D + 8 * g;
+    // queries of this wave: Q^T operands and node ancestor bitsets of its QT tiles.  A
+    // wave whose rows all lie beyond the tree's rows still queues its DMA share and
+    // joins every barrier, but computes nothing.
+    const int rw0 = row0 + wq * 32 * QT;
+    const bool wave_live = rw0 < R;
+    int rho[QT], qnode[QT], qhead[QT];
+    bf16x8 qop[QT][DS];
+    uint64_t qanc[QT];
 #pragma unroll
-      for (int s = 0; s < DS; ++s) qop[s] = *(const bf16x8*)(qp + 16 * s);
+    for (int u = 0; u < QT; ++u) {
+      rho[u] = rw0 + 32 * u + ql;
+      const int rc = rho[u] < R ? rho[u] : R - 1;
+      qnode[u] = rc / G;
+      qhead[u] = kvh * G + rc % G;
+      const __bf16* qp = a.q + (((size_t)b * a.n_max + qnode[u]) * a.Hq + qhead[u]) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qop[u][s] = *(const bf16x8*)(qp + 16 * s);
+      qanc[u] = a.anc[(size_t)b * a.n_max + qnode[u]];
     }
-    const uint64_t qanc = a.anc[(size_t)b * a.n_max + qnode];
-    wait_vmcnt<0>();      // Q and the bitset are in registers before any DMA is queued
+    wait_vmcnt<0>();      // Q and the bitsets are in registers before any DMA is queued
 
-    f32x16 o[DT];
+    f32x16 o[QT][DT];
+    float m_run[QT], l_run[QT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int u = 0; u < QT; ++u) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x16{};
+      m_run[u] = -INFINITY;
+      l_run[u] = 0.f;
+    }
 
     const size_t kv_row = (size_t)a.Hkv * D;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
     static_assert(KBLKS == (W / 2) * DMA, "half the waves cover one tile");
-    // queue the DMA of stage st into buffer buf.  Waves 0..W/2-1 fetch K rows, the
+    // queue the DMA of stage st into its buffer.  Waves 0..W/2-1 fetch K rows, the
     // others V rows; each wave covers DMA consecutive 1 KB blocks (ROWS_PER_KB rows
     // each) and each lane one 16-byte chunk, placed at its XOR-swizzled position.
     const bool dma_v = wave >= W / 2;
@@ -230,16 +274,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     const __bf16* pref_base = (dma_v ? a.v_prefix : a.k_prefix) + (size_t)off * kv_row + (size_t)kvh * D;
     const int dma_pos = lane % (ROWB / 16);
     const int dma_row = lane / (ROWB / 16);
-    auto issue = [&](int st, int buf) {
+    auto stage_kbase = [&](int st) { return (has_tree && st == 0) ? 0 : c0 + (st - has_tree) * KT; };
+    // per-lane byte offsets of this thread's DMAs within a full prefix stage (the
+    // stage's first key row is added to the uniform base)
+    uint32_t dma_off[DMA];
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int lrow = (dma_blk0 + i) * ROWS_PER_KB + dma_row;
+      dma_off[i] = (uint32_t)(((size_t)lrow * kv_row + (dma_pos ^ swz<D>(lrow)) * 8) * 2);
+    }
+    auto issue = [&](int st) {
       const bool tree = has_tree && st == 0;
-      const int kbase = tree ? 0 : c0 + (st - has_tree) * KT;
+      const int kbase = stage_kbase(st);
       const int kend = tree ? n : c1;
+      // uniform values, made explicitly scalar for the asm operands
+      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
+          lds0 + (st % NBUF) * STAGEB + (dma_v ? TILEB : 0) + dma_blk0 * 1024);
+      if (!tree && kbase + KT <= kend) {
+        const uintptr_t sbv = (uintptr_t)(pref_base + (size_t)kbase * kv_row);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sbv);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbv >> 32));
+        const void* sb = (const void*)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+        for (int i = 0; i < DMA; ++i) lds_dma16_s(sb, dma_off[i], dst0 + i * 1024);
+        return;
+      }
       const __bf16* base = tree ? tree_base : pref_base;
       const size_t rstride = tree ? (size_t)a.Hkv * D : kv_row;
-      const uint32_t dst0 = lds0 + buf * STAGEB + (dma_v ? TILEB : 0) + dma_blk0 * 1024;
       // the tree stage only fetches the 32-row subtiles that hold nodes; the others are
-      // never read (their subtiles are skipped), and fewer DMAs in flight only make the
-      // later vmcnt waits finish sooner
+      // never read (their subtiles are skipped)
       const int rows_needed = tree ? (n + 31) / 32 * 32 : KT;
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
@@ -247,13 +310,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
         const int lrow = (dma_blk0 + i) * ROWS_PER_KB + dma_row;
         const int chk = dma_pos ^ swz<D>(lrow);
         const int key = min(kbase + lrow, kend - 1);
-        lds_dma16(base + (size_t)key * rstride + chk * 8,
-                  __builtin_amdgcn_readfirstlane(dst0 + i * 1024));
+        lds_dma16(base + (size_t)key * rstride + chk * 8, dst0 + i * 1024);
       }
+    };
+    // Start of stage st: its data has landed (this wave's DMAs by vmcnt, the others'
+    // by the barrier), and every wave has finished its LDS reads of stage st-LAG, whose
+    // buffer is refilled with stage st+NBUF-LAG.  (With LAG 2, reads of stage st-1 may
+    // still be under way: the pipelined loop reads a subtile's operands ahead of its
+    // products.)
+    auto begin_stage = [&](int st) {
+      const int ahead = min(nst - 1, st < LAG ? NBUF - 1 : st + NBUF - LAG - 1) - st;
+      if (ahead <= 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<DMA>();
+      else if (ahead == 2) wait_vmcnt<2 * DMA>();
+      else wait_vmcnt<3 * DMA>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS reads are done
+      lds_barrier();
+      if (st >= LAG && st + NBUF - LAG < nst) issue(st + NBUF - LAG);
     };
 
     // lane-constant LDS byte offsets (the swizzle only depends on the low four row bits,
-    // so the subtile, k-step and buffer terms are uniform and added per use)
+    // so the subtile and buffer terms are uniform and added per use)
     int koff[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) koff[s] = ql * ROWB + (((2 * s + g) ^ swz<D>(ql)) << 4);
@@ -270,201 +347,399 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
       }
     }
 
-    // NSUB (1 or 2) 32-key subtiles processed together: S^T = K Q^T for each (the two
-    // MFMA chains interleave), one online-softmax update over all their scores, then
-    // O^T += V^T P^T with the products of both subtiles interleaved per accumulator.
-    // kMasked hides keys >= kend and, through amask (the query's ancestor bitset in the
-    // tree stage, all ones otherwise), keys off the query's root path.
-    auto subtiles = [&](auto mode_tag, auto nsub_tag, const char* kb, const char* vb, int sub0,
-                        int kbase, int kend, uint64_t amask) {
-      constexpr int MODE = decltype(mode_tag)::value;
-      constexpr int NSUB = decltype(nsub_tag)::value;
-      f32x16 sacc[NSUB];
+    // ---- building blocks on one 32-key subtile.  sub is its index within the stage,
+    // kb / vb the stage's K and V tiles in LDS.
+    struct KOps { bf16x8 v[DS]; };
+    struct VOps { bf16x8 v[2][DT]; };
+    auto load_k = [&](const char* kb, int sub) {
+      KOps k;
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) sacc[u] = f32x16{};
+      for (int s = 0; s < DS; ++s) k.v[s] = *(const bf16x8*)(kb + sub * 32 * ROWB + koff[s]);
+      return k;
+    };
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto load_v = [&](const char* vb, int sub) {
+      VOps v;
+      const uint32_t vb0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)vb +
+                           sub * 32 * ROWB;
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-          const bf16x8 kop = *(const bf16x8*)(kb + (sub0 + u * WK) * 32 * ROWB + koff[s]);
-          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[s], sacc[u], 0, 0, 0);
-        }
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-        const int key0 = kbase + (sub0 + u * WK) * 32 + 4 * g;   // key of accumulator 0
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (MODE == kMasked) {
-            const int key = key0 + 8 * (r >> 2) + (r & 3);
-            const bool vis = (key < kend) & (((amask >> (key & 63)) & 1ull) != 0ull);
-            sacc[u][r] = vis ? sacc[u][r] : -INFINITY;
-          }
-          mloc = fmaxf(mloc, sacc[u][r]);
-        }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * a.sl2;
-      // Lazy rescaling: m_run is a reference, not necessarily the maximum.  It only
-      // moves (and O, l are rescaled) when some lane's scores exceed it by more than
-      // 2^8; otherwise the weights below are at most 256, exact in fp32 and bf16.
-      if (__ballot(mloc > m_run + 8.f)) {
-        const float mnew = fmaxf(m_run, mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);   // 0 while m_run is -inf
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        l_run *= alpha;
-        m_run = mnew;
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-      // v_exp_f32 directly; weights below 2^-126 of the reference may flush to zero
-      float psum = 0.f;
-      bf16x8 pb[NSUB][2];
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[u][r] = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], a.sl2, -msub));
-          psum += sacc[u][r];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[u][0][e] = (__bf16)sacc[u][e];
-          pb[u][1][e] = (__bf16)sacc[u][8 + e];
-        }
-      }
-      l_run += psum;
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-      const uint32_t vb0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)vb;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-          for (int u = 0; u < NSUB; ++u) {
-            const uint32_t vbs = vb0 + (sub0 + u * WK) * 32 * ROWB + ks * 16 * ROWB;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(uintptr_t)(vbs + voff_lo[dt]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(uintptr_t)(vbs + voff_hi[dt]));
-            const s16x4 both[2] = {lo, hi};
-            const bf16x8 vop = *(const bf16x8*)both;
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[u][ks], o[dt], 0, 0, 0);
-          }
+          const uint32_t vbs = vb0 + ks * 16 * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vbs + voff_lo[dt]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vbs + voff_hi[dt]));
+          const s16x4 both[2] = {lo, hi};
+          v.v[ks][dt] = *(const bf16x8*)both;
         }
-      }
+      return v;
     };
-
-    auto compute = [&](int st) {
-      const int buf = st % NBUF;
-      const char* kb = smem + buf * STAGEB;
-      const char* vb = kb + TILEB;
-      const bool tree = has_tree && st == 0;
-      const int kbase = tree ? 0 : c0 + (st - has_tree) * KT;
-      const int kend = tree ? n : c1;
-      const uint64_t amask = tree ? qanc : ~0ull;
-      // The mode is fixed per stage and chosen before any MFMA is issued: a prefix
-      // stage whose keys all lie below kend needs no mask at all.  A wave that owns two
-      // subtiles of a full stage processes them as a pair.
-      constexpr int PER_WAVE = NS / WK;
-      static_assert(PER_WAVE == 1 || PER_WAVE == 2, "one or two subtiles per wave and stage");
-      if (!tree && kbase + KT <= kend) {
-        subtiles(std::integral_constant<int, kFull>{}, std::integral_constant<int, PER_WAVE>{},
-                 kb, vb, wk, kbase, kend, amask);
-      } else {
-        auto one = [&](auto j_tag) {
-          constexpr int J = decltype(j_tag)::value;
-          const int sub = wk + J * WK;
-          if (kbase + sub * 32 >= kend) return;            // wave-uniform
-          subtiles(std::integral_constant<int, kMasked>{}, std::integral_constant<int, 1>{},
-                   kb, vb, sub, kbase, kend, amask);
-        };
-        one(std::integral_constant<int, 0>{});
-        if constexpr (PER_WAVE > 1) one(std::integral_constant<int, 1>{});
-      }
+    // the same operands straight from global memory (the slow path): key kbase + k of
+    // the stage; keys at or past kend are clamped (their weights are zero)
+    auto key_row = [&](bool tree, int key, bool is_v) {
+      const __bf16* base = tree ? (is_v ? a.v_tree : a.k_tree) + ((size_t)b * a.n_max * a.Hkv + kvh) * D
+                                : (is_v ? a.v_prefix : a.k_prefix) + (size_t)off * kv_row + (size_t)kvh * D;
+      return base + (size_t)key * (tree ? (size_t)a.Hkv * D : kv_row);
     };
-
-    // ---- pipeline: up to NBUF stages in flight; stage st+NBUF-1 is queued into the
-    // buffer that stage st-1 released, right after the barrier that proves it free.
+    auto load_k_global = [&](bool tree, int k0, int kend) {
+      KOps k;
+      const __bf16* row = key_row(tree, min(k0 + ql, kend - 1), false) + 8 * g;
 #pragma unroll
-    for (int p = 0; p < NBUF; ++p)
-      if (p < nst) issue(p, p);
-    for (int st = 0; st < nst; ++st) {
-      const int ahead = min(nst - 1 - st, st == 0 ? NBUF - 1 : NBUF - 2);
-      if (ahead <= 0) wait_vmcnt<0>();
-      else if (ahead == 1) wait_vmcnt<DMA>();
-      else if (ahead == 2) wait_vmcnt<2 * DMA>();
-      else wait_vmcnt<3 * DMA>();
-      lds_barrier();
-      if (st >= 1 && st + NBUF - 1 < nst) issue(st + NBUF - 1, (st - 1) % NBUF);
-      if (wave_live) compute(st);
-    }
-    __syncthreads();
-
-    // ---- merge the key-split waves of each query group through LDS
-    if constexpr (WK > 1) {
-      float* mb = (float*)smem;
-      constexpr int PER = DT * 16 + 2;                 // floats per lane per wave
-      if (wk > 0) {
-        float* dst = mb + (size_t)(wq * (WK - 1) + wk - 1) * PER * 64;
+      for (int s = 0; s < DS; ++s) k.v[s] = *(const bf16x8*)(row + 16 * s);
+      return k;
+    };
+    auto load_v_global = [&](bool tree, int k0, int kend) {
+      // A operand lane (d, g), element e: V[key 16 ks + 8 (e >> 2) + 4 g + (e & 3)][d],
+      // the key order of the softmax weights in the B operand
+      VOps v;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dst[(dt * 16 + r) * 64 + lane] = o[dt][r];
-        dst[(DT * 16) * 64 + lane] = m_run;
-        dst[(DT * 16 + 1) * 64 + lane] = l_run;
+          for (int e = 0; e < 8; ++e) {
+            const int key = min(k0 + 16 * ks + 8 * (e >> 2) + 4 * g + (e & 3), kend - 1);
+            v.v[ks][dt][e] = key_row(tree, key, true)[32 * dt + ql];
+          }
+      return v;
+    };
+    // S^T = K Q^T for row tile U: a lane holds 16 keys of query row ql
+    auto qk = [&](auto u_tag, const KOps& k) {
+      constexpr int U = decltype(u_tag)::value;
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int i = 0; i < DS; ++i) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.v[i], qop[U][i], s, 0, 0, 0);
+      return s;
+    };
+    // O^T += V^T P^T for row tile U, with P^T the softmax weights as the B operand
+    auto pv = [&](auto u_tag, const VOps& v, const bf16x8 (&pb)[2]) {
+      constexpr int U = decltype(u_tag)::value;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          o[U][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[ks][dt], pb[ks], o[U][dt], 0, 0, 0);
+    };
+    // masking of a stage that is not full: keys >= kend and, through amask (the
+    // query's ancestor bitset in the tree stage, all ones otherwise), keys off the
+    // query's root path are -inf
+    auto apply_mask = [&](f32x16& s, int key0, int kend, uint64_t amask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + (r & 3);
+        const bool vis = (key < kend) & (((amask >> (key & 63)) & 1ull) != 0ull);
+        s[r] = vis ? s[r] : -INFINITY;
       }
-      __syncthreads();
-      if (wk == 0) {
-        for (int w = 1; w < WK; ++w) {
-          const float* src = mb + (size_t)(wq * (WK - 1) + w - 1) * PER * 64;
-          const float mo = src[(DT * 16) * 64 + lane];
-          const float lo = src[(DT * 16 + 1) * 64 + lane];
-          const float mn = fmaxf(m_run, mo);
-          const float ms = mn == -INFINITY ? 0.f : mn;
-          const float sa = exp2f(m_run - ms);
-          const float sb = exp2f(mo - ms);
+    };
+    auto lane_max = [&](const f32x16& s) {
+      float m = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+      return m * a.sl2;
+    };
+    // Fixed reference (fast path): the first subtile with a visible key sets m_run to
+    // that subtile's row maximum (both key halves of a row agree through the lane
+    // swap); after that m_run never moves and O is touched by MFMAs only.  Weights
+    // 2^(s - m_run) stay exact in bf16/fp32 up to 2^48 and cannot overflow the
+    // sums; a score beyond that sets `over`, and the wave recomputes this chunk on the
+    // slow path.
+    constexpr float kRefSpan = 48.f;
+    auto reference = [&](auto u_tag, const f32x16& s) {
+      constexpr int U = decltype(u_tag)::value;
+      const float first = max_halves(lane_max(s));
+      m_run[U] = m_run[U] == -INFINITY ? first : m_run[U];
+    };
+    // weights 2^(s*scale*log2e - m_run) as bf16 B operands; their sum (of the rounded
+    // weights, the ones the products use) is added to l and returned
+    auto weights = [&](auto u_tag, const f32x16& s, bf16x8 (&pb)[2]) {
+      constexpr int U = decltype(u_tag)::value;
+      const float msub = m_run[U] == -INFINITY ? 0.f : m_run[U];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[e], a.sl2, -msub));
+        pb[1][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 + e], a.sl2, -msub));
+      }
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, one2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, one2, psum, false);
+      }
+      l_run[U] += psum;
+      return psum;
+    };
+    // the fast path's overflow guard: a lane's 16 weights sum past 2^48 (or to inf or
+    // NaN) whenever some weight may have left the range the fixed reference carries
+    auto too_big = [&](float psum) { return !(psum <= 0x1p48f); };
+
+    // one subtile from LDS, every row tile in turn (tree and tail stages, and the
+    // one-tile layout)
+    bool over = false;
+    auto subtile_fast = [&](auto mode_tag, const char* kb, const char* vb, int sub, int kbase,
+                            int kend, bool tree) {
+      constexpr int MODE = decltype(mode_tag)::value;
+      const KOps k = load_k(kb, sub);
+      f32x16 s[QT];
+      s[0] = qk(ic<0>{}, k);
+      if constexpr (QT > 1) s[1] = qk(ic<1>{}, k);
+      const VOps v = load_v(vb, sub);
+      const int key0 = kbase + sub * 32 + 4 * g;
+      bf16x8 pb[QT][2];
+      if constexpr (MODE == kMasked) apply_mask(s[0], key0, kend, tree ? qanc[0] : ~0ull);
+      reference(ic<0>{}, s[0]);
+      over |= too_big(weights(ic<0>{}, s[0], pb[0]));
+      if constexpr (QT > 1) {
+        if constexpr (MODE == kMasked) apply_mask(s[1], key0, kend, tree ? qanc[1] : ~0ull);
+        reference(ic<1>{}, s[1]);
+        over |= too_big(weights(ic<1>{}, s[1], pb[1]));
+      }
+      pv(ic<0>{}, v, pb[0]);
+      if constexpr (QT > 1) pv(ic<1>{}, v, pb[1]);
+    };
+    auto stage_fast = [&](int st) {
+      const char* kb = smem + (st % NBUF) * STAGEB;
+      const char* vb = kb + TILEB;
+      const bool tree = has_tree && st == 0;
+      const int kbase = stage_kbase(st);
+      const int kend = tree ? n : c1;
+      const bool full = !tree && kbase + KT <= kend;
+#pragma unroll
+      for (int j = 0; j < NSW; ++j) {
+        const int sub = wk + j * WK;
+        if (kbase + sub * 32 >= kend) continue;                 // wave-uniform
+        if (full) subtile_fast(ic<kFull>{}, kb, vb, sub, kbase, kend, tree);
+        else subtile_fast(ic<kMasked>{}, kb, vb, sub, kbase, kend, tree);
+      }
+    };
+
+    // ---- pipeline over the stages: up to NBUF stages in flight
+#pragma unroll
+    for (int p = 0; p < NBUF; ++p)
+      if (p < nst) issue(p);                   // stages 0..NBUF-1 fill every buffer
+    if (!wave_live) {
+      for (int st = 0; st < nst; ++st) begin_stage(st);
+    } else if constexpr (!PIPE) {
+      for (int st = 0; st < nst; ++st) {
+        begin_stage(st);
+        stage_fast(st);
+      }
+    } else {
+      int st = 0;
+      if (has_tree) {                                           // the tree stage, masked
+        begin_stage(0);
+        stage_fast(0);
+        st = 1;
+      }
+      // Full prefix stages, two row tiles software-pipelined over the T subtiles of
+      // this wave.  Per subtile t, two phases, each issuing 16 MFMAs next to the
+      // softmax of the other tile:
+      //   X(t): QK(t+1, tile 0), PV(t, tile 0)  |  weights of tile 1 of t
+      //   Y(t): QK(t+1, tile 1), PV(t, tile 1)  |  weights of tile 0 of t+1
+      // Each subtile's K operands are read from LDS once (in X(t-1)) and its V^T
+      // operands once (in Y(t-1)), both before the barrier that releases its buffer.
+      const int T = n_full * NSW;
+      if (T > 0) {
+        auto stage_of = [&](int tt) { return st + tt / NSW; };
+        auto buf_of = [&](int tt) { return smem + (stage_of(tt) % NBUF) * STAGEB; };
+        auto sub_of = [&](int tt) { return wk + (tt % NSW) * WK; };
+        // prologue: subtile 0 through its weights, and the tile-0 scores of subtile 1
+        begin_stage(st);
+        KOps k = load_k(buf_of(0), sub_of(0));
+        VOps vprev = load_v(buf_of(0) + TILEB, sub_of(0));
+        f32x16 s0 = qk(ic<0>{}, k);
+        f32x16 s1 = qk(ic<1>{}, k);
+        bf16x8 p0prev[2], p1prev[2];
+        reference(ic<0>{}, s0);
+        reference(ic<1>{}, s1);
+        over |= too_big(weights(ic<0>{}, s0, p0prev));
+        over |= too_big(weights(ic<1>{}, s1, p1prev));
+        const int t1 = min(1, T - 1);
+        if (T > 1 && 1 % NSW == 0) begin_stage(stage_of(1));
+        k = load_k(buf_of(t1), sub_of(t1));
+        s0 = qk(ic<0>{}, k);
+        // Round tt (two phases), each phase 16 MFMAs beside one tile's softmax whose
+        // scores were produced a phase earlier, and products fed by weights two phases
+        // old -- so no instruction waits on the matrix core's latest results:
+        //   A: QK(tt, tile 1), PV(tt-1, tile 0)    | weights of tile 0 of tt
+        //   B: QK(tt+1, tile 0), PV(tt-1, tile 1)  | weights of tile 1 of tt
+        // The LDS reads of K(tt+1) and V(tt) are spread over the two phases.  Two
+        // register sets alternate between rounds (the loop is unrolled by two), so the
+        // operands of consecutive rounds never need copying.
+        auto round = [&](int tt, const KOps& kc, const VOps& vp, const bf16x8 (&p0p)[2],
+                         const bf16x8 (&p1p)[2], KOps& kn, VOps& vc, bf16x8 (&p0)[2],
+                         bf16x8 (&p1)[2]) {
+          const int tn = min(tt + 1, T - 1);
+          if (tt + 1 < T && (tt + 1) % NSW == 0) begin_stage(stage_of(tt + 1));
+          __builtin_amdgcn_sched_barrier(0);
+          // phase A (the K(tt+1) reads spread between its products)
+          kn = load_k(buf_of(tn), sub_of(tn));
+          s1 = qk(ic<1>{}, kc);
+          pv(ic<0>{}, vp, p0p);
+          over |= too_big(weights(ic<0>{}, s0, p0));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // phase B (the V(tt) reads spread between its products)
+          vc = load_v(buf_of(tt) + TILEB, sub_of(tt));
+          s0 = qk(ic<0>{}, kn);
+          pv(ic<1>{}, vp, p1p);
+          over |= too_big(weights(ic<1>{}, s1, p1));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        KOps k2;
+        VOps v2;
+        bf16x8 q0[2], q1[2];
+        int tt = 1;
+        for (; tt + 1 < T; tt += 2) {
+          round(tt, k, vprev, p0prev, p1prev, k2, v2, q0, q1);
+          round(tt + 1, k2, v2, q0, q1, k, vprev, p0prev, p1prev);
+        }
+        if (tt < T) {
+          round(tt, k, vprev, p0prev, p1prev, k2, v2, q0, q1);
+          pv(ic<0>{}, v2, q0);
+          pv(ic<1>{}, v2, q1);
+        } else {
+          pv(ic<0>{}, vprev, p0prev);
+          pv(ic<1>{}, vprev, p1prev);
+        }
+        st += n_full;
+      }
+      if (st < nst) {                                           // the partial last stage
+        begin_stage(st);
+        stage_fast(st);
+      }
+    }
+
+    // ---- slow path: a score left the fixed reference's range.  This wave recomputes
+    // its rows of the chunk from global memory in two passes (exact row maximum first,
+    // then the weighted sum against it), without barriers.
+    if (__ballot(over)) {
+      auto for_subtiles = [&](auto&& body) {
+        for (int st = 0; st < nst; ++st) {
+          const bool tree = has_tree && st == 0;
+          const int kbase = stage_kbase(st);
+          const int kend = tree ? n : c1;
+          for (int j = 0; j < NSW; ++j) {
+            const int k0 = kbase + (wk + j * WK) * 32;
+            if (k0 < kend) body(tree, k0, kend);
+          }
+        }
+      };
+      float mx[QT];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) mx[u] = -INFINITY;
+      for_subtiles([&](bool tree, int k0, int kend) {
+        const KOps k = load_k_global(tree, k0, kend);
+        f32x16 s = qk(ic<0>{}, k);
+        apply_mask(s, k0 + 4 * g, kend, tree ? qanc[0] : ~0ull);
+        mx[0] = fmaxf(mx[0], lane_max(s));
+        if constexpr (QT > 1) {
+          s = qk(ic<1>{}, k);
+          apply_mask(s, k0 + 4 * g, kend, tree ? qanc[1] : ~0ull);
+          mx[1] = fmaxf(mx[1], lane_max(s));
+        }
+      });
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x16{};
+        m_run[u] = max_halves(mx[u]);
+        l_run[u] = 0.f;
+      }
+      for_subtiles([&](bool tree, int k0, int kend) {
+        const KOps k = load_k_global(tree, k0, kend);
+        const VOps v = load_v_global(tree, k0, kend);
+        bf16x8 pb[2];
+        f32x16 s = qk(ic<0>{}, k);
+        apply_mask(s, k0 + 4 * g, kend, tree ? qanc[0] : ~0ull);
+        weights(ic<0>{}, s, pb);
+        pv(ic<0>{}, v, pb);
+        if constexpr (QT > 1) {
+          s = qk(ic<1>{}, k);
+          apply_mask(s, k0 + 4 * g, kend, tree ? qanc[1] : ~0ull);
+          weights(ic<1>{}, s, pb);
+          pv(ic<1>{}, v, pb);
+        }
+      });
+    }
+    // ---- every wave parks its rows (unnormalised O, reference m, sum l) in LDS, then
+    // the whole workgroup combines the key-split waves of each row and writes the
+    // chunk's output with coalesced stores: the final rows when the sequence's prefix
+    // fits in one chunk, else unnormalised partials for attn_combine.
+    __syncthreads();                                   // the stage ring is free now
+    float* ob = (float*)smem;
+    float2* mlb = (float2*)(ob + OB_FLOATS);
+    {
+      float lt[QT];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) lt[u] = sum_halves(l_run[u]);
+      if (wave_live) {
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          float* orow = ob + ((wave * QT + u) * 32 + ql) * OSTR;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * sa + src[(dt * 16 + r) * 64 + lane] * sb;
-          l_run = l_run * sa + lo * sb;
-          m_run = mn;
+            for (int r4 = 0; r4 < 4; ++r4)
+              *(f32x4*)(orow + 32 * dt + 8 * r4 + 4 * g) =
+                  f32x4{o[u][dt][4 * r4], o[u][dt][4 * r4 + 1], o[u][dt][4 * r4 + 2], o[u][dt][4 * r4 + 3]};
+          if (g == 0) mlb[(wave * QT + u) * 32 + ql] = make_float2(m_run[u], lt[u]);
         }
       }
     }
-
-    // ---- output of this chunk: the final row when the sequence's prefix fits in one
-    // chunk, else an unnormalised partial for attn_combine
-    if (wk == 0 && wave_live && rho < R) {
-      const float ltot = l_run + __shfl_xor(l_run, 32);
-      const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
+    __syncthreads();
+    const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < a.rows_per_wg * D4; idx += kAttnThreads) {
+      const int i = idx / D4;                          // row within the workgroup
+      const int d = (idx % D4) * 4;
+      const int rho_i = row0 + i;
+      if (rho_i >= R) continue;                        // padding rows (chunk 0 zero-fills them)
+      const int qg = i / (32 * QT);
+      const int slot_w = (i / 32) % QT * 32 + i % 32;  // (tile, row) within a wave
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WK; ++w) M = fmaxf(M, mlb[(qg * WK + w) * QT * 32 + slot_w].x);
+      const float ms = M == -INFINITY ? 0.f : M;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < WK; ++w) {
+        const float2 ml = mlb[(qg * WK + w) * QT * 32 + slot_w];
+        const float sc = __builtin_amdgcn_exp2f(ml.x - ms);      // 0 for a wave without keys
+        acc += *(const f32x4*)(ob + ((qg * WK + w) * QT * 32 + slot_w) * OSTR + d) * sc;
+        lsum += ml.y * sc;
+      }
+      const int node = rho_i / G;
+      const int head = kvh * G + rho_i % G;
       if (nc == 1) {
-        const size_t orow = ((size_t)b * a.n_max + qnode) * a.Hq + qhead;
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        __bf16* op = a.out + orow * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * dt + 8 * r4 + 4 * g;
-            __bf16 ob[4] = {(__bf16)(o[dt][4 * r4] * inv), (__bf16)(o[dt][4 * r4 + 1] * inv),
-                            (__bf16)(o[dt][4 * r4 + 2] * inv), (__bf16)(o[dt][4 * r4 + 3] * inv)};
-            *(s16x4*)(op + d) = *(const s16x4*)ob;
-          }
-        if (a.lse && g == 0) a.lse[orow] = ltot > 0.f ? (m_run + log2f(ltot)) * kLn2 : 0.f;
+        const size_t orow = ((size_t)b * a.n_max + node) * a.Hq + head;
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        __bf16 ob4[4] = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
+                         (__bf16)(acc[3] * inv)};
+        *(s16x4*)(a.out + orow * D + d) = *(const s16x4*)ob4;
+        if (a.lse && d == 0) a.lse[orow] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : 0.f;
       } else {
-        const size_t slot = ((size_t)unit * a.n_chunks + chunk) * a.rows_per_wg + wq * 32 + ql;
-        float* po = a.part_o + slot * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * dt + 8 * r4 + 4 * g;
-            *(f32x4*)(po + d) = f32x4{o[dt][4 * r4], o[dt][4 * r4 + 1], o[dt][4 * r4 + 2],
-                                      o[dt][4 * r4 + 3]};
-          }
-        if (g == 0) a.part_ml[slot] = make_float2(m_run, ltot);
+        const size_t slot = ((size_t)unit * a.n_chunks + chunk) * a.rows_per_wg + i;
+        *(f32x4*)(a.part_o + slot * D + d) = acc;
+        if (d == 0) a.part_ml[slot] = make_float2(M, lsum);
       }
     }
   }
@@ -638,9 +913,11 @@ __global__ __launch_bounds__(128) void attn_f32(
 
 template <int D>
 static void launch_bf16(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
-  if (p.wk == 4) hipLaunchKernelGGL((attn_bf16<D, 2, 4>), dim3(p.grid), dim3(kAttnThreads), 0, stream, a);
-  else if (p.wk == 2) hipLaunchKernelGGL((attn_bf16<D, 4, 2>), dim3(p.grid), dim3(kAttnThreads), 0, stream, a);
-  else hipLaunchKernelGGL((attn_bf16<D, 8, 1>), dim3(p.grid), dim3(kAttnThreads), 0, stream, a);
+  const dim3 grid(p.grid), block(kAttnThreads);
+  if (p.wk == 4 && p.qt == 1) hipLaunchKernelGGL((attn_bf16<D, 1, 4, 1>), grid, block, 0, stream, a);
+  else if (p.wk == 4) hipLaunchKernelGGL((attn_bf16<D, 1, 4, 2>), grid, block, 0, stream, a);
+  else if (p.wk == 2) hipLaunchKernelGGL((attn_bf16<D, 2, 2, 2>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((attn_bf16<D, 4, 1, 2>), grid, block, 0, stream, a);
   if (p.n_chunks > 1) {
     const int rows = a.B * a.n_max * a.Hq;
     hipLaunchKernelGGL(attn_combine<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
