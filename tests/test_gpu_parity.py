@@ -270,6 +270,29 @@ def test_attn_deterministic():
     assert torch.equal(a1.view(torch.int16), a2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def test_attn_workspace_reused():
+    """Consecutive calls on one workspace (whose chunk counters each call must leave
+    cleared) give the same, correct results -- also with different trees in between."""
+    inp, parent, nn = synth.random_attention_case(11, 2, 16, 16, 128, (2048, 1500), (26, 40))
+    d = attn_device_inputs(inp)
+    ws = tv.attn_workspace(torch.bfloat16, 2, 64, 16, 16, 128, 2048)
+    ref, _ = oracle.tree_verify_attn(inp.f32("q"), inp.f32("k_tree"), inp.f32("v_tree"),
+                                     inp.f32("k_prefix"), inp.f32("v_prefix"),
+                                     inp.prefix_offsets, parent, nn)
+    par, nnd = dev_i32(parent), dev_i32(nn)
+    anc, _, _, _ = tv.tree_build(par, nnd)
+    outs = []
+    for _ in range(3):
+        out, _, _ = tv.tree_verify_attn(d["q"], d["k_tree"], d["v_tree"], d["k_prefix"],
+                                        d["v_prefix"], d["offsets"], nnd, anc, 2048, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    for o in outs:
+        ok, msg = attn_close(o, ref, "workspace reuse")
+        assert ok, msg
+    assert np.array_equal(outs[0], outs[2])
+
+
 def test_attn_workload2_full():
     w = synth.WORKLOADS[2]
     parent, nn = synth.static_tree(w)

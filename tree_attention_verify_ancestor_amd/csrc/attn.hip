@@ -236,6 +236,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     // joins every barrier, but computes nothing.
     const int rw0 = row0 + wq * 32 * QT;
     const bool wave_live = rw0 < R;
+    const bool live1 = rw0 + 32 < R;                 // the wave's second tile has rows
     int rho[QT], qnode[QT], qhead[QT];
     bf16x8 qop[QT][DS];
     uint64_t qanc[QT];
@@ -250,7 +251,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
       for (int s = 0; s < DS; ++s) qop[u][s] = *(const bf16x8*)(qp + 16 * s);
       qanc[u] = a.anc[(size_t)b * a.n_max + qnode[u]];
     }
-    wait_vmcnt<0>();      // Q and the bitsets are in registers before any DMA is queued
 
     f32x16 o[QT][DT];
     float m_run[QT], l_run[QT];
@@ -477,26 +477,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     // one subtile from LDS, every row tile in turn (tree and tail stages, and the
     // one-tile layout)
     bool over = false;
-    auto subtile_fast = [&](auto mode_tag, const char* kb, const char* vb, int sub, int kbase,
-                            int kend, bool tree) {
+    auto subtile_fast = [&](auto mode_tag, auto ntile_tag, const char* kb, const char* vb, int sub,
+                            int kbase, int kend, bool tree) {
       constexpr int MODE = decltype(mode_tag)::value;
+      constexpr int NT = decltype(ntile_tag)::value;
       const KOps k = load_k(kb, sub);
-      f32x16 s[QT];
+      f32x16 s[NT];
       s[0] = qk(ic<0>{}, k);
-      if constexpr (QT > 1) s[1] = qk(ic<1>{}, k);
+      if constexpr (NT > 1) s[1] = qk(ic<1>{}, k);
       const VOps v = load_v(vb, sub);
       const int key0 = kbase + sub * 32 + 4 * g;
-      bf16x8 pb[QT][2];
+      bf16x8 pb[NT][2];
       if constexpr (MODE == kMasked) apply_mask(s[0], key0, kend, tree ? qanc[0] : ~0ull);
       reference(ic<0>{}, s[0]);
       over |= too_big(weights(ic<0>{}, s[0], pb[0]));
-      if constexpr (QT > 1) {
+      if constexpr (NT > 1) {
         if constexpr (MODE == kMasked) apply_mask(s[1], key0, kend, tree ? qanc[1] : ~0ull);
         reference(ic<1>{}, s[1]);
         over |= too_big(weights(ic<1>{}, s[1], pb[1]));
       }
       pv(ic<0>{}, v, pb[0]);
-      if constexpr (QT > 1) pv(ic<1>{}, v, pb[1]);
+      if constexpr (NT > 1) pv(ic<1>{}, v, pb[1]);
     };
     auto stage_fast = [&](int st) {
       const char* kb = smem + (st % NBUF) * STAGEB;
@@ -509,8 +510,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
       for (int j = 0; j < NSW; ++j) {
         const int sub = wk + j * WK;
         if (kbase + sub * 32 >= kend) continue;                 // wave-uniform
-        if (full) subtile_fast(ic<kFull>{}, kb, vb, sub, kbase, kend, tree);
-        else subtile_fast(ic<kMasked>{}, kb, vb, sub, kbase, kend, tree);
+        // a second tile whose rows all lie past the tree's rows is skipped
+        if (QT > 1 && live1) {
+          if (full) subtile_fast(ic<kFull>{}, ic<QT>{}, kb, vb, sub, kbase, kend, tree);
+          else subtile_fast(ic<kMasked>{}, ic<QT>{}, kb, vb, sub, kbase, kend, tree);
+        } else {
+          if (full) subtile_fast(ic<kFull>{}, ic<1>{}, kb, vb, sub, kbase, kend, tree);
+          else subtile_fast(ic<kMasked>{}, ic<1>{}, kb, vb, sub, kbase, kend, tree);
+        }
       }
     };
 
@@ -518,14 +525,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < NBUF; ++p)
       if (p < nst) issue(p);                   // stages 0..NBUF-1 fill every buffer
+    // Q and the bitsets (loaded before the DMAs, so their latencies overlap) are in
+    // registers; this also covers the first stages, needed next in any case
+    wait_vmcnt<0>();
     if (!wave_live) {
       for (int st = 0; st < nst; ++st) begin_stage(st);
-    } else if constexpr (!PIPE) {
+    } else if (!live1 || !PIPE) {
       for (int st = 0; st < nst; ++st) {
         begin_stage(st);
         stage_fast(st);
       }
-    } else {
+    } else if constexpr (PIPE) {
       int st = 0;
       if (has_tree) {                                           // the tree stage, masked
         begin_stage(0);
@@ -693,6 +703,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
       if (wave_live) {
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
+          if (u == 1 && !live1) break;
           float* orow = ob + ((wave * QT + u) * 32 + ql) * OSTR;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
