@@ -321,8 +321,13 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   PoolEntry* pool = (PoolEntry*)(seq + sizeof(SeqHeader));
   const ChunkRec* recs = (const ChunkRec*)(seq + rec_off);
 
-  __shared__ __attribute__((aligned(16))) float s_score[kPoolMax + 16];
+  __shared__ float s_score[kTopKMax * kTopKMax];
+  __shared__ uint32_t s_key[kPoolMax];
+  __shared__ uint8_t s_dep[kPoolMax];
   __shared__ short s_pos[kPoolMax];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_wtot[kSelWaves];
+  __shared__ int s_sel_digit, s_sel_before;
   __shared__ int s_tok[kTopKMax * kTopKMax];
   __shared__ int s_front[kTopKMax];
   __shared__ int s_kept[TV_MAX_NODES];
@@ -448,26 +453,93 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     int keep = 0;
     if (st == TV_SEQ_OK) {
       keep = min(s_m - 1, count);
-      // scores padded to a multiple of 16 with -inf, which never ranks above a score
-      const int count16 = (count + 15) & ~15;
-      for (int c = tid; c < count16; c += kSelThreads) {
-        s_score[c] = c < count ? pool[c].score : -INFINITY;
-        if (c < count) s_pos[c] = -1;
-      }
-      __syncthreads();
+      // the pool as order-preserving keys of the scores (and the depths) in LDS
       for (int c = tid; c < count; c += kSelThreads) {
-        const float sc = s_score[c];
-        int rank = 0;
-        for (int o = 0; o < count16 && rank < keep; o += 16) {
-          const f32x4* q4 = (const f32x4*)(s_score + o);
-          const f32x4 w[4] = {q4[0], q4[1], q4[2], q4[3]};
-#pragma unroll
-          for (int j = 0; j < 16; ++j) rank += better(w[j >> 2][j & 3], o + j, sc, c);
-        }
-        if (rank < keep) s_kept[atomicAdd(&s_nkept, 1)] = c;
+        const PoolEntry e = pool[c];
+        s_key[c] = fkey(e.score);
+        s_dep[c] = (uint8_t)e.depth;
+        s_pos[c] = -1;
       }
       __syncthreads();
-      if (tid < keep) s_kdep[tid] = pool[s_kept[tid]].depth;
+      if (keep == count) {                               // everything is kept
+        for (int c = tid; c < count; c += kSelThreads) s_kept[c] = c;
+        if (tid == 0) s_nkept = count;
+        __syncthreads();
+      } else if (keep > 0) {
+        // T = the keep-th largest key, by radix selection 8 bits at a time from the top;
+        // `need` ends as the number of entries equal to T that are kept
+        uint32_t T = 0, tmask = 0;
+        int need = keep;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          if (tid < 256) s_hist[tid] = 0u;
+          __syncthreads();
+          for (int c = tid; c < count; c += kSelThreads) {
+            const uint32_t u = s_key[c];
+            if ((u & tmask) == T) atomicAdd(&s_hist[(u >> shift) & 255u], 1u);
+          }
+          __syncthreads();
+          if (wave == 0) {
+            // lane l holds the digits 255-4l .. 252-4l, scanned from the top
+            uint32_t h[4], sum = 0;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              h[j] = s_hist[255 - 4 * lane - j];
+              sum += h[j];
+            }
+            uint32_t incl = sum;
+            for (int o = 1; o < kWave; o <<= 1) {
+              const uint32_t t = __shfl_up(incl, o);
+              if (lane >= o) incl += t;
+            }
+            const uint32_t before = incl - sum;
+            if (before < (uint32_t)need && (uint32_t)need <= incl) {
+              uint32_t cum = before;
+              int d = 255 - 4 * lane;
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                if (cum + h[j] >= (uint32_t)need) {
+                  d = 255 - 4 * lane - j;
+                  break;
+                }
+                cum += h[j];
+              }
+              s_sel_digit = d;
+              s_sel_before = (int)cum;
+            }
+          }
+          __syncthreads();
+          T |= (uint32_t)s_sel_digit << shift;
+          tmask |= 255u << shift;
+          need -= s_sel_before;
+          __syncthreads();
+        }
+        // kept: keys above T, and the `need` earliest-created entries equal to T (the rank
+        // among those comes from an in-order scan of per-thread tie counts)
+        const int seg = (count + kSelThreads - 1) / kSelThreads;
+        const int cs = tid * seg;
+        int ties = 0;
+        for (int j = 0; j < seg; ++j)
+          if (cs + j < count && s_key[cs + j] == T) ++ties;
+        int incl = ties;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        if (lane == kWave - 1) s_wtot[wave] = incl;
+        __syncthreads();
+        int rank = incl - ties;
+        for (int w = 0; w < wave; ++w) rank += s_wtot[w];
+        for (int j = 0; j < seg; ++j) {
+          const int c = cs + j;
+          if (c >= count) break;
+          const uint32_t u = s_key[c];
+          const bool kept = u > T || (u == T && rank < need);
+          if (u == T) ++rank;
+          if (kept) s_kept[atomicAdd(&s_nkept, 1)] = c;
+        }
+        __syncthreads();
+      }
+      if (tid < keep) s_kdep[tid] = s_dep[s_kept[tid]];
       __syncthreads();
       // output position: root first, then by (depth, creation)
       if (tid < keep) {
