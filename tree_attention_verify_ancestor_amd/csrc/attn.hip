@@ -11,20 +11,25 @@
 // group share it -- a dense contraction per byte, done on bf16 MFMA.
 //
 // bf16 path (gfx950):
-//   attn_bf16_partial  grid = (sequence, KV head, key chunk, row block), XCD-aware.
-//     A workgroup of 4 waves owns up to 32*QT*(4/WK) query rows (rows = node*G + head
-//     in group) and one chunk of prefix keys; chunk 0 also owns the tree keys.  Each
-//     stage stages 32*NS keys of K and V from HBM through registers into XOR-swizzled
-//     LDS (double-buffered).  Each wave computes S^T = K Q^T with
-//     v_mfma_f32_32x32x16_bf16, so a lane holds 16 keys of one query; the ancestor
-//     bitset of that query's node sits in two registers and masks the tree stage
-//     only.  Online softmax runs in the log2 domain (scale*log2e folded into one
-//     multiply, exp2), and O^T += V^T P^T reuses the S^T accumulator as the B operand
-//     directly; V^T comes from LDS through ds_read_b64_tr_b16.  With WK > 1 the four
-//     waves split each stage's keys and merge their (m, l, O) through LDS.  The
-//     result per row and chunk is an unnormalised fp32 partial plus (max, sum).
-//   attn_combine       one wave per output row merges the chunk partials, writes
-//     bf16 out and the natural-log lse, and zeroes padding rows.
+//   attn_bf16      grid = (sequence, KV head, row block, key chunk), XCD-aware.  A
+//     workgroup owns up to 256 query rows of one KV head (rows = node * G + head in the
+//     group) and one chunk of prefix keys; chunk 0 also owns the tree keys.  Stages of
+//     64 or 128 keys of K and V go from HBM straight into XOR-swizzled LDS by LDS DMA
+//     (global_load_lds), up to four stages in flight.  A wave computes S^T = K Q^T on
+//     v_mfma_f32_32x32x16_bf16 (a lane holds 16 keys of one query row), masks the tree
+//     stage with the query node's 64-bit ancestor bitset, turns scores into weights
+//     2^(s - m) against a fixed per-row reference m (the row maximum of its first
+//     visible subtile; an exact two-pass recompute takes over if a weight could pass
+//     2^48) and accumulates O^T += V^T P^T, reading V^T with ds_read_b64_tr_b16.
+//     Shapes: up to 32 rows, 4 waves split each stage's keys; up to 64 rows, the same
+//     with two row tiles per wave; up to 128 rows, 8 waves as 4 row groups x 2 key
+//     halves; beyond, 8 waves of one 32-row tile each.  With 8 waves two share each
+//     SIMD, so one wave's softmax (vector ALUs) runs beside the other's products.
+//     Key-split waves merge their (m, l, O) through LDS.  The output per row and chunk
+//     is the final bf16 row when one chunk covers the prefix, else an unnormalised
+//     fp32 partial plus (m, l).
+//   attn_combine   one wave per output row merges the chunk partials, writes bf16 out
+//     and the natural-log lse.
 // fp32 path: attn_f32, one workgroup per output row on the vector ALUs (the
 // fp32 workloads are small correctness cases).
 #include <math.h>
@@ -60,14 +65,13 @@ struct AttnArgs {
 };
 
 struct AttnPlan {
-  int wq, wk, qt, rows_per_wg, n_rb, chunk_keys, n_chunks, units, total_wgs, grid;
+  int waves, wq, wk, qt, rows_per_wg, n_rb, chunk_keys, n_chunks, units, total_wgs, grid;
   size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
-constexpr int kWaves = 4;
 constexpr int kMaxChunks = 32;                       // key chunks per work unit (merge width)
-constexpr int kAttnThreads = 64 * kWaves;
-constexpr int kLdsBudget = 128 * 1024;
+constexpr int kLdsBudget = 128 * 1024;               // the ring of prefix stages
+constexpr int kLdsMax = 160 * 1024;                  // LDS of one CU
 
 __host__ __device__ constexpr int stage_keys(int wk) { return 32 * (wk > 2 ? wk : 2); }
 __host__ __device__ constexpr int stage_bytes(int D, int wk) { return 2 * stage_keys(wk) * 2 * D; }
@@ -75,16 +79,20 @@ __host__ __device__ constexpr int n_buffers(int D, int wk) {
   return kLdsBudget / stage_bytes(D, wk) < 4 ? kLdsBudget / stage_bytes(D, wk) : 4;
 }
 
-// Work split of one workgroup (4 waves): WQ query groups x WK key splits, each wave
-// owning QT tiles of 32 rows (rows = node * G + head within the group).
+// Work split of one workgroup: WQ query groups x WK key splits, each wave owning QT
+// tiles of 32 rows (rows = node * G + head within the group).  Small row counts use
+// four waves that split the keys; from 128 rows on, eight waves of one tile each, two
+// per SIMD, so that one wave's softmax runs on the vector ALUs while the other's
+// products occupy the matrix core.
 static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_prefix) {
   AttnPlan p{};
   const int G = Hq / Hkv;
   const int R = n_max * G;
   if (R <= 32) { p.wq = 1; p.wk = 4; p.qt = 1; }
   else if (R <= 64) { p.wq = 1; p.wk = 4; p.qt = 2; }
-  else if (R <= 128) { p.wq = 2; p.wk = 2; p.qt = 2; }
-  else { p.wq = 4; p.wk = 1; p.qt = 2; }
+  else if (R <= 128) { p.wq = 4; p.wk = 2; p.qt = 1; }
+  else { p.wq = 8; p.wk = 1; p.qt = 1; }
+  p.waves = p.wq * p.wk;
   p.rows_per_wg = 32 * p.qt * p.wq;
   p.n_rb = (R + p.rows_per_wg - 1) / p.rows_per_wg;
   const int kt = stage_keys(p.wk);
@@ -160,9 +168,10 @@ using ic = std::integral_constant<int, N>;
 enum StageMode { kFull = 0, kMasked = 1 };
 
 template <int D, int WQ, int WK, int QT>
-__global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   constexpr int W = WQ * WK;
-  static_assert(W == kWaves, "four waves per workgroup");
+  constexpr int NT = 64 * W;
+  static_assert(W == 4 || W == 8, "four or eight waves per workgroup");
   constexpr int KT = stage_keys(WK);            // keys per stage
   constexpr int NS = KT / 32;                   // 32-key subtiles per stage
   constexpr int NSW = NS / WK;                  // subtiles per wave and stage
@@ -170,25 +179,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
   constexpr int TILEB = KT * ROWB;              // K (or V) bytes per stage
   constexpr int STAGEB = 2 * TILEB;
   constexpr int NBUF = n_buffers(D, WK);
-  constexpr int DMA = STAGEB / (kAttnThreads * 16);   // 16-byte LDS DMAs per thread per stage
+  constexpr int DMA = STAGEB / (NT * 16);             // 16-byte LDS DMAs per thread per stage
   constexpr int ROWS_PER_KB = 1024 / ROWB;
   constexpr int KBLKS = TILEB / 1024;
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
-  // Two row tiles per wave allow the software pipeline that overlaps one tile's
-  // softmax (vector ALUs) with the other tile's matrix products.
-  constexpr bool PIPE = QT == 2 && NBUF >= 3;
-  constexpr int LAG = PIPE ? 2 : 1;            // stages between a buffer's use and its refill
-  static_assert(DMA * kAttnThreads * 16 == STAGEB, "stage must split into 1 KB DMA blocks");
+  static_assert(DMA * NT * 16 == STAGEB, "stage must split into 1 KB DMA blocks");
   static_assert(NBUF >= 2 && NBUF <= 4, "two to four stage buffers");
+  static_assert(NBUF * DMA < 64, "the DMAs in flight fit the vmcnt counter");
   static_assert(NSW * WK == NS && NSW >= 1, "whole subtiles per wave");
   static_assert(QT == 1 || QT == 2, "one or two row tiles per wave");
 
-  // LDS: the stage ring, reused at the end for the rows of all waves (fp32, padded)
+  // LDS: the ring of NBUF prefix stages, then, with a ring of two, an area of its own
+  // for the tree stage's K and V (at most 64 rows each), so that the tree stage does
+  // not hold back a prefix stage.  All of it is reused at the end for the rows of all
+  // waves (fp32, padded).
+  constexpr int TREE_TILEB = TV_MAX_NODES * ROWB;
+  constexpr int RING = NBUF * STAGEB;
+  constexpr bool SEP_TREE = NBUF == 2 && RING + 2 * TREE_TILEB <= kLdsMax;
   constexpr int OSTR = D + 4;
   constexpr int OB_FLOATS = W * QT * 32 * OSTR;
   constexpr int OUT_BYTES = OB_FLOATS * 4 + W * QT * 32 * 8;
-  constexpr int SMEM = NBUF * STAGEB > OUT_BYTES ? NBUF * STAGEB : OUT_BYTES;
+  constexpr int STAGE_AREA = RING + (SEP_TREE ? 2 * TREE_TILEB : 0);
+  constexpr int SMEM = STAGE_AREA > OUT_BYTES ? STAGE_AREA : OUT_BYTES;
+  static_assert(SMEM <= kLdsMax, "LDS of one workgroup");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   // ---- work item.  The order puts KV heads fastest, then row blocks, then chunks:
@@ -275,100 +289,122 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     const int dma_pos = lane % (ROWB / 16);
     const int dma_row = lane / (ROWB / 16);
     auto stage_kbase = [&](int st) { return (has_tree && st == 0) ? 0 : c0 + (st - has_tree) * KT; };
-    // per-lane byte offsets of this thread's DMAs within a full prefix stage (the
-    // stage's first key row is added to the uniform base)
-    uint32_t dma_off[DMA];
-#pragma unroll
-    for (int i = 0; i < DMA; ++i) {
-      const int lrow = (dma_blk0 + i) * ROWS_PER_KB + dma_row;
-      dma_off[i] = (uint32_t)(((size_t)lrow * kv_row + (dma_pos ^ swz<D>(lrow)) * 8) * 2);
-    }
-    auto issue = [&](int st) {
+    // LDS byte offsets of stage st's K tile and of its V tile from the K tile: the tree
+    // stage has its own area when it fits, the prefix stages cycle through the ring
+    const int extra = SEP_TREE && has_tree ? 1 : 0;       // stages outside the ring
+    auto k_tile = [&](int st) {
+      return (SEP_TREE && has_tree && st == 0) ? RING : ((st - extra) % NBUF) * STAGEB;
+    };
+    auto v_tile = [&](int st) { return (SEP_TREE && has_tree && st == 0) ? TREE_TILEB : TILEB; };
+    // per-lane byte offset of this thread's first DMA within a full prefix stage (the
+    // stage's first key row is added to the uniform base).  DMA i reads ROWS_PER_KB * i
+    // rows further on (a uniform term) at a chunk whose index differs by XOR with i & 3
+    // for D = 128 (the swizzle of the row) and not at all for D = 64.
+    static_assert(DMA % 4 == 0 || D == 64, "the chunk XOR repeats every four DMAs");
+    const uint32_t dma_off0 = (uint32_t)(((size_t)(dma_blk0 * ROWS_PER_KB + dma_row) * kv_row +
+                                          (dma_pos ^ swz<D>(dma_blk0 * ROWS_PER_KB + dma_row)) * 8) * 2);
+    auto issue = [&](int st) __attribute__((always_inline)) {
       const bool tree = has_tree && st == 0;
       const int kbase = stage_kbase(st);
       const int kend = tree ? n : c1;
       // uniform values, made explicitly scalar for the asm operands
       const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
-          lds0 + (st % NBUF) * STAGEB + (dma_v ? TILEB : 0) + dma_blk0 * 1024);
+          lds0 + k_tile(st) + (dma_v ? v_tile(st) : 0) + dma_blk0 * 1024);
       if (!tree && kbase + KT <= kend) {
         const uintptr_t sbv = (uintptr_t)(pref_base + (size_t)kbase * kv_row);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sbv);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbv >> 32));
-        const void* sb = (const void*)(((uint64_t)hi << 32) | lo);
 #pragma unroll
-        for (int i = 0; i < DMA; ++i) lds_dma16_s(sb, dma_off[i], dst0 + i * 1024);
+        for (int i = 0; i < DMA; ++i) {
+          const uint64_t sbi = (((uint64_t)hi << 32) | lo) + (uint64_t)i * ROWS_PER_KB * kv_row * 2;
+          const uint32_t ilo = __builtin_amdgcn_readfirstlane((uint32_t)sbi);
+          const uint32_t ihi = __builtin_amdgcn_readfirstlane((uint32_t)(sbi >> 32));
+          lds_dma16_s((const void*)(((uint64_t)ihi << 32) | ilo),
+                      D == 128 ? dma_off0 ^ ((i & 3) << 4) : dma_off0, dst0 + i * 1024);
+        }
         return;
       }
       const __bf16* base = tree ? tree_base : pref_base;
       const size_t rstride = tree ? (size_t)a.Hkv * D : kv_row;
+      const uintptr_t sbv = (uintptr_t)(base + (size_t)kbase * rstride);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sbv);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(sbv >> 32));
+      const void* sb = (const void*)(((uint64_t)hi << 32) | lo);
       // the tree stage only fetches the 32-row subtiles that hold nodes; the others are
-      // never read (their subtiles are skipped)
+      // never read (their subtiles are skipped).  Rows past the stage's last key repeat
+      // that key (their weights are zero).
       const int rows_needed = tree ? (n + 31) / 32 * 32 : KT;
+      const int last = kend - 1 - kbase;
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
         if ((dma_blk0 + i) * ROWS_PER_KB >= rows_needed) continue;      // wave-uniform
         const int lrow = (dma_blk0 + i) * ROWS_PER_KB + dma_row;
         const int chk = dma_pos ^ swz<D>(lrow);
-        const int key = min(kbase + lrow, kend - 1);
-        lds_dma16(base + (size_t)key * rstride + chk * 8, dst0 + i * 1024);
+        lds_dma16_s(sb, (uint32_t)(min(lrow, last) * rstride * 2) + chk * 16, dst0 + i * 1024);
       }
     };
     // Start of stage st: its data has landed (this wave's DMAs by vmcnt, the others'
-    // by the barrier), and every wave has finished its LDS reads of stage st-LAG, whose
-    // buffer is refilled with stage st+NBUF-LAG.  (With LAG 2, reads of stage st-1 may
-    // still be under way: the pipelined loop reads a subtile's operands ahead of its
-    // products.)
-    auto begin_stage = [&](int st) {
-      const int ahead = min(nst - 1, st < LAG ? NBUF - 1 : st + NBUF - LAG - 1) - st;
+    // by the barrier), and every wave has finished its LDS reads of stage st-1; a
+    // prefix stage's buffer is then refilled with stage st+NBUF-1.  The DMAs complete
+    // in issue order, so stage st has landed once at most the DMAs of the stages issued
+    // after it are outstanding: stages up to extra+NBUF-1 at the start, then one more
+    // per refill.  (The tree stage may issue fewer DMAs; it is always the oldest.)
+    auto begin_stage = [&](int st) __attribute__((always_inline)) {
+      const int ahead = min(nst - 1, max(extra + NBUF - 1, st + NBUF - 2)) - st;
       if (ahead <= 0) wait_vmcnt<0>();
       else if (ahead == 1) wait_vmcnt<DMA>();
       else if (ahead == 2) wait_vmcnt<2 * DMA>();
-      else wait_vmcnt<3 * DMA>();
+      else if (ahead == 3) wait_vmcnt<3 * DMA>();
+      else wait_vmcnt<NBUF * DMA>();                       // the tree stage, NBUF = 4
       __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS reads are done
       lds_barrier();
-      if (st >= LAG && st + NBUF - LAG < nst) issue(st + NBUF - LAG);
+      if (st - extra >= 1 && st + NBUF - 1 < nst) issue(st + NBUF - 1);
     };
 
-    // lane-constant LDS byte offsets (the swizzle only depends on the low four row bits,
-    // so the subtile and buffer terms are uniform and added per use)
-    int koff[DS];
-#pragma unroll
-    for (int s = 0; s < DS; ++s) koff[s] = ql * ROWB + (((2 * s + g) ^ swz<D>(ql)) << 4);
-    uint32_t voff_lo[DT], voff_hi[DT];
+    // lane-constant LDS byte offsets of the first K and V^T operand reads.  The others
+    // differ from them by XOR in the chunk bits of the row (the swizzle only depends on
+    // the low four row bits), and every subtile and buffer base is a multiple of the
+    // row size, so one register per operand serves all reads:
+    //   K operand s:       (base + koff0) ^ (s << 5)
+    //   V^T operand dt:    A = (base + voff0) ^ (dt << 6) for rows 0-7 of the 16-key
+    //                      step, (A ^ VHI) + 8 rows for rows 8-15
+    const uint32_t koff0 = ql * ROWB + ((g ^ swz<D>(ql)) << 4);
+    uint32_t voff0;
     {
       const int s16 = lane & 15;
       const int rlo = 4 * g + (s16 >> 2);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int chk = 4 * dt + 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
-        const int half = (s16 & 1) << 3;
-        voff_lo[dt] = rlo * ROWB + ((chk ^ swz<D>(rlo)) << 4) + half;
-        voff_hi[dt] = (rlo + 8) * ROWB + ((chk ^ swz<D>(rlo + 8)) << 4) + half;
-      }
+      const int chk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+      voff0 = rlo * ROWB + ((chk ^ swz<D>(rlo)) << 4) + ((s16 & 1) << 3);
     }
+    constexpr uint32_t VHI = D == 128 ? 32 : 0;   // swz(row + 8) ^ swz(row), in bytes
 
     // ---- building blocks on one 32-key subtile.  sub is its index within the stage,
     // kb / vb the stage's K and V tiles in LDS.
     struct KOps { bf16x8 v[DS]; };
     struct VOps { bf16x8 v[2][DT]; };
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto lds_addr = [](const char* p) {
+      return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+    };
     auto load_k = [&](const char* kb, int sub) {
       KOps k;
+      const uint32_t a0 = lds_addr(kb) + sub * 32 * ROWB + koff0;
 #pragma unroll
-      for (int s = 0; s < DS; ++s) k.v[s] = *(const bf16x8*)(kb + sub * 32 * ROWB + koff[s]);
+      for (int s = 0; s < DS; ++s) k.v[s] = *(lds_bf16x8*)(uintptr_t)(a0 ^ (s << 5));
       return k;
     };
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     auto load_v = [&](const char* vb, int sub) {
       VOps v;
-      const uint32_t vb0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)vb +
-                           sub * 32 * ROWB;
+      const uint32_t a0 = lds_addr(vb) + sub * 32 * ROWB + voff0;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint32_t vbs = vb0 + ks * 16 * ROWB;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vbs + voff_lo[dt]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(vbs + voff_hi[dt]));
+          const uint32_t lo_a = (a0 ^ (dt << 6)) + ks * 16 * ROWB;
+          const uint32_t hi_a = ((a0 ^ (dt << 6)) ^ VHI) + 8 * ROWB + ks * 16 * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)lo_a);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)hi_a);
           const s16x4 both[2] = {lo, hi};
           v.v[ks][dt] = *(const bf16x8*)both;
         }
@@ -423,13 +459,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     // masking of a stage that is not full: keys >= kend and, through amask (the
     // query's ancestor bitset in the tree stage, all ones otherwise), keys off the
     // query's root path are -inf
+    // A lane's keys are key0 + 8 (r >> 2) + (r & 3), all within 28 of key0 (and below 64
+    // in the tree stage, where key0 < 64 too), so one 32-bit mask holds them all.
     auto apply_mask = [&](f32x16& s, int key0, int kend, uint64_t amask) {
+      const int lim = kend - key0;
+      const uint32_t below = lim >= 32 ? ~0u : (lim <= 0 ? 0u : (1u << lim) - 1u);
+      const uint32_t vis = (uint32_t)(amask >> (key0 & 63)) & below;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + (r & 3);
-        const bool vis = (key < kend) & (((amask >> (key & 63)) & 1ull) != 0ull);
-        s[r] = vis ? s[r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        s[r] = (vis & (1u << (8 * (r >> 2) + (r & 3)))) ? s[r] : -INFINITY;
     };
     auto lane_max = [&](const f32x16& s) {
       float m = s[0];
@@ -477,31 +515,51 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     // one subtile from LDS, every row tile in turn (tree and tail stages, and the
     // one-tile layout)
     bool over = false;
+    bool ref_open = true;        // some row of the wave has no reference yet (wave-uniform)
     auto subtile_fast = [&](auto mode_tag, auto ntile_tag, const char* kb, const char* vb, int sub,
                             int kbase, int kend, bool tree) {
       constexpr int MODE = decltype(mode_tag)::value;
       constexpr int NT = decltype(ntile_tag)::value;
+      // eight waves: subtiles strictly one after another (the other wave of the SIMD
+      // provides the overlap), which keeps the live registers within 256
+      if constexpr (W == 8) __builtin_amdgcn_sched_barrier(0);
       const KOps k = load_k(kb, sub);
       f32x16 s[NT];
+      // with two waves per SIMD, a wave raises its priority for its products so that
+      // they issue back to back while the other wave works on the vector ALUs
+      if constexpr (W == 8) __builtin_amdgcn_s_setprio(1);
       s[0] = qk(ic<0>{}, k);
       if constexpr (NT > 1) s[1] = qk(ic<1>{}, k);
+      if constexpr (W == 8) __builtin_amdgcn_s_setprio(0);
+      // with two waves per SIMD the other wave hides the V^T read latency: read V^T
+      // only after the products that consume K, so K and V^T never occupy registers
+      // together
+      if constexpr (W == 8) __builtin_amdgcn_sched_barrier(0);
       const VOps v = load_v(vb, sub);
       const int key0 = kbase + sub * 32 + 4 * g;
       bf16x8 pb[NT][2];
       if constexpr (MODE == kMasked) apply_mask(s[0], key0, kend, tree ? qanc[0] : ~0ull);
-      reference(ic<0>{}, s[0]);
-      over |= too_big(weights(ic<0>{}, s[0], pb[0]));
-      if constexpr (NT > 1) {
+      if constexpr (NT > 1)
         if constexpr (MODE == kMasked) apply_mask(s[1], key0, kend, tree ? qanc[1] : ~0ull);
-        reference(ic<1>{}, s[1]);
-        over |= too_big(weights(ic<1>{}, s[1], pb[1]));
+      if (ref_open) {
+        reference(ic<0>{}, s[0]);
+        bool open = m_run[0] == -INFINITY;
+        if constexpr (NT > 1) {
+          reference(ic<1>{}, s[1]);
+          open |= m_run[1] == -INFINITY;
+        }
+        ref_open = __ballot(open) != 0;
       }
+      over |= too_big(weights(ic<0>{}, s[0], pb[0]));
+      if constexpr (NT > 1) over |= too_big(weights(ic<1>{}, s[1], pb[1]));
+      if constexpr (W == 8) __builtin_amdgcn_s_setprio(1);
       pv(ic<0>{}, v, pb[0]);
       if constexpr (NT > 1) pv(ic<1>{}, v, pb[1]);
+      if constexpr (W == 8) __builtin_amdgcn_s_setprio(0);
     };
     auto stage_fast = [&](int st) {
-      const char* kb = smem + (st % NBUF) * STAGEB;
-      const char* vb = kb + TILEB;
+      const char* kb = smem + k_tile(st);
+      const char* vb = kb + v_tile(st);
       const bool tree = has_tree && st == 0;
       const int kbase = stage_kbase(st);
       const int kend = tree ? n : c1;
@@ -521,117 +579,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
       }
     };
 
-    // ---- pipeline over the stages: up to NBUF stages in flight
-#pragma unroll
-    for (int p = 0; p < NBUF; ++p)
-      if (p < nst) issue(p);                   // stages 0..NBUF-1 fill every buffer
-    // Q and the bitsets (loaded before the DMAs, so their latencies overlap) are in
-    // registers; this also covers the first stages, needed next in any case
+    // ---- pipeline over the stages: the tree stage and up to NBUF prefix stages in
+    // flight.  Q and the bitsets were loaded before the first stage's DMAs; one wait
+    // for all of them (stage 0 is needed first in any case) also tells the compiler
+    // that its loads are done -- it counts only its own loads and would otherwise wait
+    // for every outstanding DMA before each use of Q inside the loop.  Then the other
+    // stages are queued.
+    if (nst > 0) issue(0);
     wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 1; p < NBUF + 1; ++p)
+      if (p < nst && p < NBUF + extra) issue(p);
     if (!wave_live) {
       for (int st = 0; st < nst; ++st) begin_stage(st);
-    } else if (!live1 || !PIPE) {
+    } else {
       for (int st = 0; st < nst; ++st) {
-        begin_stage(st);
-        stage_fast(st);
-      }
-    } else if constexpr (PIPE) {
-      int st = 0;
-      if (has_tree) {                                           // the tree stage, masked
-        begin_stage(0);
-        stage_fast(0);
-        st = 1;
-      }
-      // Full prefix stages, two row tiles software-pipelined over the T subtiles of
-      // this wave.  Per subtile t, two phases, each issuing 16 MFMAs next to the
-      // softmax of the other tile:
-      //   X(t): QK(t+1, tile 0), PV(t, tile 0)  |  weights of tile 1 of t
-      //   Y(t): QK(t+1, tile 1), PV(t, tile 1)  |  weights of tile 0 of t+1
-      // Each subtile's K operands are read from LDS once (in X(t-1)) and its V^T
-      // operands once (in Y(t-1)), both before the barrier that releases its buffer.
-      const int T = n_full * NSW;
-      if (T > 0) {
-        auto stage_of = [&](int tt) { return st + tt / NSW; };
-        auto buf_of = [&](int tt) { return smem + (stage_of(tt) % NBUF) * STAGEB; };
-        auto sub_of = [&](int tt) { return wk + (tt % NSW) * WK; };
-        // prologue: subtile 0 through its weights, and the tile-0 scores of subtile 1
-        begin_stage(st);
-        KOps k = load_k(buf_of(0), sub_of(0));
-        VOps vprev = load_v(buf_of(0) + TILEB, sub_of(0));
-        f32x16 s0 = qk(ic<0>{}, k);
-        f32x16 s1 = qk(ic<1>{}, k);
-        bf16x8 p0prev[2], p1prev[2];
-        reference(ic<0>{}, s0);
-        reference(ic<1>{}, s1);
-        over |= too_big(weights(ic<0>{}, s0, p0prev));
-        over |= too_big(weights(ic<1>{}, s1, p1prev));
-        const int t1 = min(1, T - 1);
-        if (T > 1 && 1 % NSW == 0) begin_stage(stage_of(1));
-        k = load_k(buf_of(t1), sub_of(t1));
-        s0 = qk(ic<0>{}, k);
-        // Round tt (two phases), each phase 16 MFMAs beside one tile's softmax whose
-        // scores were produced a phase earlier, and products fed by weights two phases
-        // old -- so no instruction waits on the matrix core's latest results:
-        //   A: QK(tt, tile 1), PV(tt-1, tile 0)    | weights of tile 0 of tt
-        //   B: QK(tt+1, tile 0), PV(tt-1, tile 1)  | weights of tile 1 of tt
-        // The LDS reads of K(tt+1) and V(tt) are spread over the two phases.  Two
-        // register sets alternate between rounds (the loop is unrolled by two), so the
-        // operands of consecutive rounds never need copying.
-        auto round = [&](int tt, const KOps& kc, const VOps& vp, const bf16x8 (&p0p)[2],
-                         const bf16x8 (&p1p)[2], KOps& kn, VOps& vc, bf16x8 (&p0)[2],
-                         bf16x8 (&p1)[2]) {
-          const int tn = min(tt + 1, T - 1);
-          if (tt + 1 < T && (tt + 1) % NSW == 0) begin_stage(stage_of(tt + 1));
-          __builtin_amdgcn_sched_barrier(0);
-          // phase A (the K(tt+1) reads spread between its products)
-          kn = load_k(buf_of(tn), sub_of(tn));
-          s1 = qk(ic<1>{}, kc);
-          pv(ic<0>{}, vp, p0p);
-          over |= too_big(weights(ic<0>{}, s0, p0));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          // phase B (the V(tt) reads spread between its products)
-          vc = load_v(buf_of(tt) + TILEB, sub_of(tt));
-          s0 = qk(ic<0>{}, kn);
-          pv(ic<1>{}, vp, p1p);
-          over |= too_big(weights(ic<1>{}, s1, p1));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        KOps k2;
-        VOps v2;
-        bf16x8 q0[2], q1[2];
-        int tt = 1;
-        for (; tt + 1 < T; tt += 2) {
-          round(tt, k, vprev, p0prev, p1prev, k2, v2, q0, q1);
-          round(tt + 1, k2, v2, q0, q1, k, vprev, p0prev, p1prev);
-        }
-        if (tt < T) {
-          round(tt, k, vprev, p0prev, p1prev, k2, v2, q0, q1);
-          pv(ic<0>{}, v2, q0);
-          pv(ic<1>{}, v2, q1);
-        } else {
-          pv(ic<0>{}, vprev, p0prev);
-          pv(ic<1>{}, vprev, p1prev);
-        }
-        st += n_full;
-      }
-      if (st < nst) {                                           // the partial last stage
         begin_stage(st);
         stage_fast(st);
       }
@@ -718,11 +680,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     __syncthreads();
     const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
     constexpr int D4 = D / 4;
-    for (int idx = tid; idx < a.rows_per_wg * D4; idx += kAttnThreads) {
+    // only the rows that hold tree nodes (chunk 0 zero-fills the others); unrolled, so
+    // that the LDS reads of several rows are in flight together
+    constexpr int ITEMS = 32 * QT * WQ * D4 / NT;
+    static_assert(ITEMS * NT == 32 * QT * WQ * D4, "whole items per thread");
+    const int live_items = min(a.rows_per_wg, R - row0) * D4;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * NT;
+      if (idx >= live_items) break;
       const int i = idx / D4;                          // row within the workgroup
       const int d = (idx % D4) * 4;
       const int rho_i = row0 + i;
-      if (rho_i >= R) continue;                        // padding rows (chunk 0 zero-fills them)
       const int qg = i / (32 * QT);
       const int slot_w = (i / 32) % QT * 32 + i % 32;  // (tile, row) within a wave
       float M = -INFINITY;
@@ -738,9 +707,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
         acc += *(const f32x4*)(ob + ((qg * WK + w) * QT * 32 + slot_w) * OSTR + d) * sc;
         lsum += ml.y * sc;
       }
-      const int node = rho_i / G;
-      const int head = kvh * G + rho_i % G;
       if (nc == 1) {
+        const int node = rho_i / G;
+        const int head = kvh * G + rho_i % G;
         const size_t orow = ((size_t)b * a.n_max + node) * a.Hq + head;
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         __bf16 ob4[4] = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
@@ -763,7 +732,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16(AttnArgs a) {
     constexpr int V4 = D / 4;
     const int rows_total = a.n_max * G;
     const int first_dead = seq_ok ? R : 0;
-    for (int idx = tid; idx < a.rows_per_wg * V4; idx += kAttnThreads) {
+    for (int idx = tid; idx < a.rows_per_wg * V4; idx += NT) {
       const int rho = row0 + idx / V4;
       if (rho < first_dead || rho >= rows_total) continue;
       const size_t orow = ((size_t)b * a.n_max + rho / G) * a.Hq + kvh * G + rho % G;
@@ -924,11 +893,11 @@ __global__ __launch_bounds__(128) void attn_f32(
 
 template <int D>
 static void launch_bf16(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(p.grid), block(kAttnThreads);
+  const dim3 grid(p.grid), block(64 * p.waves);
   if (p.wk == 4 && p.qt == 1) hipLaunchKernelGGL((attn_bf16<D, 1, 4, 1>), grid, block, 0, stream, a);
   else if (p.wk == 4) hipLaunchKernelGGL((attn_bf16<D, 1, 4, 2>), grid, block, 0, stream, a);
-  else if (p.wk == 2) hipLaunchKernelGGL((attn_bf16<D, 2, 2, 2>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((attn_bf16<D, 4, 1, 2>), grid, block, 0, stream, a);
+  else if (p.wk == 2) hipLaunchKernelGGL((attn_bf16<D, 4, 2, 1>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((attn_bf16<D, 8, 1, 1>), grid, block, 0, stream, a);
   if (p.n_chunks > 1) {
     const int rows = a.B * a.n_max * a.Hq;
     hipLaunchKernelGGL(attn_combine<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
