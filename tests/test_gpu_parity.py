@@ -196,6 +196,9 @@ SMALL_ATTN = [  # (B, Hq, Hkv, D, prefix lengths, node counts)
     (2, 16, 2, 64, (5000, 300), (64, 50)),
     (1, 32, 32, 128, (2048,), (26,)),
     (5, 64, 8, 128, (700, 10, 1500, 64, 0), (64, 3, 64, 32, 64)),
+    # 65..128 rows per KV head (eight waves as four row groups x two key halves)
+    (2, 4, 2, 64, (300, 1000), (64, 40)),
+    (1, 6, 3, 128, (777,), (50,)),
 ]
 
 
@@ -205,6 +208,15 @@ def test_attn_small_bf16(case):
     inp, parent, nn = synth.random_attention_case(abs(hash(case)) % 10000, B, Hq, Hkv, D, lens, ns,
                                                   dtype="bf16", std=0.5)
     _check_attn(inp, parent, nn, f"case {case}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_attn_few_rows(D):
+    """At most 32 rows per KV head (n_max 16, one query head per KV head): four waves
+    split each stage's keys and merge through LDS."""
+    inp, parent, nn = synth.random_attention_case(4242 + D, 3, 2, 2, D, (100, 0, 2500), (16, 9, 16),
+                                                  dtype="bf16", std=0.5, n_max=16)
+    _check_attn(inp, parent, nn, f"few rows D={D}")
 
 
 @pytest.mark.parametrize("std", [0.5, 2.0])

@@ -9,7 +9,8 @@
 // One wavefront per sequence, lane i <-> node i: each lane tests its own token
 // against the target's token after its parent, a ballot gathers the passing nodes,
 // a node is reachable when its ancestor bitset lies inside that ballot, and a wave
-// maximum over (depth, -index) picks the deepest reachable node.
+// maximum over (depth, -index) picks the deepest reachable node.  All of a lane's
+// inputs are loaded at once; values of other nodes come by lane shuffles.
 #include "tv_internal.h"
 
 namespace tv {
@@ -23,10 +24,17 @@ __global__ __launch_bounds__(256) void tree_accept_kernel(
   const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (b >= B) return;
   const int i = lane_id();
-  const int n = n_nodes[b];
   const size_t row = (size_t)b * n_max;
+  // every load up front (one memory round trip); lanes past n_max read node 0
+  const int il = i < n_max ? i : 0;
+  const int n = n_nodes[b];
+  const uint64_t a_in = anc[row + il];
+  const int p_in = parent[row + il];
+  const int tok = token[row + il];
+  const int tgt = target_next[row + il];
+  const int d_in = depth[row + il];
   bool valid = n >= 1 && n <= n_max;
-  if (valid) valid = anc[row] == 1ull;        // the root's set is exactly {0} in a built tree
+  if (valid) valid = shfl_u64(a_in, 0) == 1ull;  // the root's set is exactly {0} in a built tree
   if (!valid) {
     if (i == 0) {
       accept_len[b] = -1;
@@ -37,31 +45,27 @@ __global__ __launch_bounds__(256) void tree_accept_kernel(
     return;
   }
   const bool in_tree = i < n;
-  bool hit = (i == 0);
-  uint64_t a = 0;
-  int key = -1;
-  if (in_tree) {
-    a = anc[row + i];
-    if (i > 0) {
-      int p = parent[row + i];
-      p = p < 0 ? 0 : (p >= n ? n - 1 : p);     // stays in bounds even for malformed input
-      hit = token[row + i] == target_next[row + p];
-    }
-  }
+  // the target's token after node p sits in lane p (p stays in bounds even for
+  // malformed input)
+  const int p = p_in < 0 ? 0 : (p_in >= n ? n - 1 : p_in);
+  const int tgt_parent = __shfl(tgt, p);
+  const bool hit = (i == 0) || (in_tree && tok == tgt_parent);
+  const uint64_t a = in_tree ? a_in : 0ull;
   const uint64_t passing = __ballot(in_tree && hit) | 1ull;
+  int key = -1;
   if (in_tree && (a & ~passing) == 0) {
-    int d = depth[row + i];
-    d = d < 0 ? 0 : (d > 63 ? 63 : d);
+    const int d = d_in < 0 ? 0 : (d_in > 63 ? 63 : d_in);
     key = (d << 8) | (63 - i);
   }
   key = wave_max_i32(key);
   const int best = 63 - (key & 0xFF);
   const int alen = key >> 8;
   const uint64_t best_set = shfl_u64(a, best) & ~1ull;   // chosen path without the root
+  const int bonus = __shfl(tgt, best);
   if (i == 0) {
     accept_len[b] = alen;
     best_node[b] = best;
-    bonus_token[b] = target_next[row + best];
+    bonus_token[b] = bonus;
   }
   if (path && i < n_max) {
     if ((best_set >> i) & 1ull) {
