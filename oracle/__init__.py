@@ -25,7 +25,8 @@ Pages this oracle follows (cited by title and section throughout):
   verification trees and the harness": the attention mask lets every token see
   the shared prefix, its ancestors and itself, hiding siblings and other
   branches; verification follows the accepted path and then continues with the
-  target's own token.
+  target's own token; the harness then keeps the accepted continuation and frees
+  the rejected KV-cache entries.
 
 Precision: attention is computed in float64 from the exact float32 upcast of the
 inputs (the pages fix no precision).  The tree-expansion scores are the one place
@@ -42,9 +43,10 @@ from .tree import tree_build, validate_parents, path_to_root, STATUS_OK, STATUS_
 from .attention import tree_verify_attn, tree_mask
 from .expand import expand_rerank, ExpandResult
 from .accept import tree_accept
+from .compact import kv_compact, kept_nodes
 
 __all__ = [
     "tree_build", "validate_parents", "path_to_root", "tree_verify_attn", "tree_mask",
-    "expand_rerank", "ExpandResult", "tree_accept",
+    "expand_rerank", "ExpandResult", "tree_accept", "kv_compact", "kept_nodes",
     "STATUS_OK", "STATUS_BAD_PARENT", "STATUS_SECOND_ROOT", "STATUS_BAD_N", "STATUS_NONFINITE",
 ]

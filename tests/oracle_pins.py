@@ -492,6 +492,91 @@ def pin_accept_closed_forms():
     return bool(ok)
 
 
+# ----------------------------------------------------------------------------- compaction
+
+def _compact_case(seed, B=5, n_max=64, Hkv=2, D=8, rows=600):
+    rng = np.random.default_rng(seed)
+    parent = np.full((B, n_max), -1, np.int32)
+    nn = rng.integers(1, n_max + 1, size=B).astype(np.int32)
+    for b in range(B):
+        for i in range(1, int(nn[b])):
+            parent[b, i] = rng.integers(0, i)
+    tok = rng.integers(0, 5, size=(B, n_max)).astype(np.int32)       # small vocabulary: many hits
+    tgt = rng.integers(0, 5, size=(B, n_max)).astype(np.int32)
+    kt = rng.standard_normal((B, n_max, Hkv, D)).astype(np.float32)
+    vt = rng.standard_normal((B, n_max, Hkv, D)).astype(np.float32)
+    kd = rng.standard_normal((rows, Hkv, D)).astype(np.float32)
+    vd = rng.standard_normal((rows, Hkv, D)).astype(np.float32)
+    dst = (np.arange(B) * (rows // B)).astype(np.int64)
+    return parent, nn, tok, tgt, kt, vt, kd, vd, dst
+
+
+def pin_compact_chain():
+    """A chain whose every draft token is the target's: the whole tree, in order, and
+    nothing past it."""
+    parent, nn, tok, tgt, kt, vt, kd, vd, dst = _compact_case(5, B=1)
+    n = 20
+    nn[0] = n
+    parent[0, :] = -1
+    parent[0, 1:n] = np.arange(n - 1)
+    tgt[0, :n - 1] = tok[0, 1:n]
+    alen, best, _, path = oracle.tree_accept(parent, tok, tgt, nn)
+    if alen[0] != n - 1 or best[0] != n - 1:
+        return False
+    k2, v2 = oracle.kv_compact(kt, vt, path, alen, kd, vd, dst)
+    return (np.array_equal(k2[:n], kt[0, :n]) and np.array_equal(v2[:n], vt[0, :n]) and
+            np.array_equal(k2[n:], kd[n:]) and np.array_equal(v2[n:], vd[n:]))
+
+
+def pin_compact_root_only():
+    """No draft token matches: only the root's row is written."""
+    parent, nn, tok, tgt, kt, vt, kd, vd, dst = _compact_case(6, B=1)
+    nn[0] = 10
+    parent[0, :10] = [-1, 0, 0, 1, 1, 2, 3, 3, 4, 8]
+    tgt[0] = -7
+    alen, _, _, path = oracle.tree_accept(parent, tok, tgt, nn)
+    if alen[0] != 0:
+        return False
+    k2, v2 = oracle.kv_compact(kt, vt, path, alen, kd, vd, dst)
+    return (np.array_equal(k2[0], kt[0, 0]) and np.array_equal(v2[0], vt[0, 0]) and
+            np.array_equal(k2[1:], kd[1:]) and np.array_equal(v2[1:], vd[1:]))
+
+
+def pin_compact_root_path(seed=7):
+    """Row 0 is the root; each further row's node is the child of the previous row's
+    node on the way to the chosen node (an independent walk up from the chosen node);
+    nothing else of the destination changes."""
+    parent, nn, tok, tgt, kt, vt, kd, vd, dst = _compact_case(seed)
+    alen, best, _, path = oracle.tree_accept(parent, tok, tgt, nn)
+    k2, v2 = oracle.kv_compact(kt, vt, path, alen, kd, vd, dst)
+    written = np.zeros(kd.shape[0], bool)
+    for b in range(parent.shape[0]):
+        chain = [int(best[b])]
+        while chain[-1] != 0:
+            chain.append(int(parent[b, chain[-1]]))
+        chain = chain[::-1]
+        if len(chain) != int(alen[b]) + 1:
+            return False
+        for j, node in enumerate(chain):
+            r = int(dst[b]) + j
+            if not (np.array_equal(k2[r], kt[b, node]) and np.array_equal(v2[r], vt[b, node])):
+                return False
+            written[r] = True
+    return np.array_equal(k2[~written], kd[~written]) and np.array_equal(v2[~written], vd[~written])
+
+
+def pin_compact_edges():
+    """A rejected tree (accept_len -1) copies nothing; rows past the buffer are skipped."""
+    parent, nn, tok, tgt, kt, vt, kd, vd, dst = _compact_case(10, B=2, rows=40)
+    path = np.full((2, 64), -1, np.int32)
+    path[1, :5] = [1, 2, 3, 4, 5]
+    alen = np.array([-1, 5], np.int32)
+    dst = np.array([0, 37], np.int64)                                    # rows 37..42: 3 fit
+    k2, _ = oracle.kv_compact(kt, vt, path, alen, kd, vd, dst)
+    return (np.array_equal(k2[:37], kd[:37]) and np.array_equal(k2[37], kt[1, 0]) and
+            np.array_equal(k2[38], kt[1, 1]) and np.array_equal(k2[39], kt[1, 2]))
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -511,6 +596,10 @@ ALL_PINS = {
     "expand_nonfinite": pin_expand_nonfinite,
     "accept_bruteforce": pin_accept_bruteforce,
     "accept_closed_forms": pin_accept_closed_forms,
+    "compact_chain": pin_compact_chain,
+    "compact_root_only": pin_compact_root_only,
+    "compact_root_path": pin_compact_root_path,
+    "compact_edges": pin_compact_edges,
 }
 
 

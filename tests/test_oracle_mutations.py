@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.accept
 import oracle.attention
+import oracle.compact
 import oracle.expand
 import oracle.tree
 import oracle_pins
@@ -82,6 +83,12 @@ MUTATIONS = {
     "accept: compares with the node's own target": [
         (oracle.accept, "node_passes", lambda par, tok, tgt, j: int(tok[j]) == int(tgt[j]))],
     "accept: walk drops the node itself": [(oracle.accept, "path_to_root", _walk_without_self)],
+    "compact: root not kept": [
+        (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [int(row[j]) for j in range(n)])],
+    "compact: path kept leaf first": [
+        (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n)][::-1])],
+    "compact: one node short": [
+        (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }
 
 

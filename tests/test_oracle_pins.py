@@ -75,3 +75,8 @@ def test_dynamic_workload_tree_small():
     assert res.status[0] == 0 and res.n_nodes[0] == 60 and not res.indeterminate[0]
     anc, depth, pos, st = oracle.tree_build(res.parent, res.n_nodes, None)
     assert st[0] == 0 and depth[0].max() <= 6
+
+
+@pytest.mark.parametrize("seed", [8, 9, 10])
+def test_compact_root_path_more_seeds(seed):
+    assert oracle_pins.pin_compact_root_path(seed)
