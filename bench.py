@@ -15,7 +15,9 @@ not what is timed) and the graphs are replayed.  The dominant kernel's roofline 
 the tree_verify_attn call: its algorithmic bytes (prefix K/V + tree K/V + Q + O)
 divided by its average duration, measured with HIP events on its stream around
 graph replays of back-to-back attention calls over the rotated copies.  The CPU
-baseline is the plain oracle timed on a bounded sample on the host cores.
+baseline is the plain oracle timed on a bounded sample on the host cores.  The KV
+compaction that follows acceptance (tree_kv_compact, outside the step) is timed the
+same way and reported beside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -248,8 +250,43 @@ def gpu_leg(args, inp):
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / (args.attn_reps * R)
+
+    # KV compaction after acceptance (outside the step): each copy's accepted
+    # continuation into a destination cache, launches back to back
+    comp_in, rows_written = [], 0
+    for c in copies:
+        par, nn, tok = tree_of(c)
+        anc, depth, _, _ = tv.tree_build(par, nn, prefix_len)
+        alen, _, _, path = tv.tree_accept(par, depth, anc, nn, tok, tgt_d)
+        comp_in.append((c, path, alen))
+        rows_written += int((alen.clamp(min=-1) + 1).sum().item())
+    k_dst = torch.empty((w.B * w.n_max, w.Hkv, w.D), dtype=dt, device=dev)
+    v_dst = torch.empty_like(k_dst)
+    dst_row = torch.arange(w.B, dtype=torch.int64, device=dev) * w.n_max
+    compact = lambda c, path, alen: tv.tree_kv_compact(c["k_tree"], c["v_tree"], path, alen,
+                                                       k_dst, v_dst, dst_row)
+    with torch.cuda.stream(side):
+        for ci in comp_in:
+            compact(*ci)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        for ci in comp_in:
+            compact(*ci)
+    cg.replay()
+    torch.cuda.synchronize()
+    a0.record(stream)
+    for _ in range(args.attn_reps):
+        cg.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    compact_ms = a0.elapsed_time(a1) / (args.attn_reps * R)
+    el = 2 if w.dtype == "bf16" else 4
+    compact_bytes = rows_written / R * w.Hkv * w.D * el * 2 * 2      # K and V, read and write
     return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, copies=R,
-                tree=tree_host)
+                tree=tree_host, compact_ms=compact_ms, compact_bytes=compact_bytes,
+                compact_rows=rows_written / R)
 
 
 def copy_reference(mib):
@@ -355,6 +392,9 @@ def main():
                      "bytes_per_launch": abytes, "launch_ms": g["attn_ms"],
                      "mfma_tflops": mfma_tflops, "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},
         "ms_per_step_wall": g["step_ms_wall"],
+        "kv_compact": {"us_per_call": g["compact_ms"] * 1e3, "rows_per_call": g["compact_rows"],
+                       "bytes_per_call": g["compact_bytes"],
+                       "GB/s": g["compact_bytes"] / (g["compact_ms"] * 1e-3) / 1e9},
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_leg(args, inp, g["tree"])

@@ -193,6 +193,36 @@ tv_status tree_accept(int B, int n_max, const int32_t* parent, const int32_t* de
                       const int32_t* target_next, int32_t* accept_len, int32_t* best_node,
                       int32_t* bonus_token, int32_t* path, hipStream_t stream);
 
+/*
+ * tree_kv_compact -- the accepted continuation's K/V into the KV cache.
+ * [EAGLE-4] "verification trees and the harness": after verification the harness
+ * keeps the accepted continuation, frees the rejected KV-cache entries and starts
+ * the next round.  The continuation is the root (node 0, the target's last token:
+ * queried in this pass, not yet cached) and the accepted path, root to leaf.
+ *
+ *   dt             TV_BF16 or TV_F32 (the element type of all four K/V buffers)
+ *   k_tree, v_tree [B][n_max][Hkv][D]  per-node K/V of this pass (tree_verify_attn's
+ *                                     k_tree / v_tree)
+ *   path           int32 [B][n_max]   tree_accept's path (accepted nodes without the
+ *                                     root, in index order = root-to-leaf order)
+ *   accept_len     int32 [B]          tree_accept's accept_len; < 0 copies nothing
+ *   k_dst, v_dst   [dst_rows][Hkv][D] destination rows (e.g. the cache after each
+ *                                     sequence's prefix), caller-owned
+ *   dst_row        int64 [B]          destination row of sequence b's root; rows
+ *                                     dst_row[b] .. dst_row[b] + accept_len[b] are
+ *                                     written: row 0 <- node 0, row j <- path[j-1]
+ *   dst_rows       host int64         rows in k_dst / v_dst; rows outside
+ *                                     [0, dst_rows) and path entries outside
+ *                                     [0, n_max) are skipped
+ * No other destination row is touched.  Rows of different sequences must not
+ * overlap (they are written concurrently).  Needs Hkv*D*element size a multiple of
+ * 16 bytes and 16-byte aligned buffers (else TV_ERR_UNSUPPORTED).
+ */
+tv_status tree_kv_compact(tv_dtype dt, int B, int n_max, int Hkv, int D, const void* k_tree,
+                          const void* v_tree, const int32_t* path, const int32_t* accept_len,
+                          void* k_dst, void* v_dst, const int64_t* dst_row, int64_t dst_rows,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

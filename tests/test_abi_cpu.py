@@ -148,3 +148,24 @@ def test_product_code_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def _compact(L, dt=1, B=2, n_max=64, Hkv=2, D=128, kt=P, vt=P, path=P, alen=P, kd=P, vd=P, dst=P,
+             rows=100):
+    return L.tree_kv_compact(dt, B, n_max, Hkv, D, kt, vt, path, alen, kd, vd, dst, rows, Z)
+
+
+def test_kv_compact_validation(L):
+    assert _compact(L, dt=7) == DTYPE
+    assert _compact(L, B=0) == SHAPE
+    assert _compact(L, n_max=65) == SHAPE
+    assert _compact(L, Hkv=0) == SHAPE
+    assert _compact(L, rows=-1) == SHAPE
+    assert _compact(L, kt=Z) == NULL
+    assert _compact(L, path=Z) == NULL
+    assert _compact(L, alen=Z) == NULL
+    assert _compact(L, dst=Z) == NULL
+    assert _compact(L, kd=Z) == NULL
+    assert _compact(L, Hkv=1, D=4) == UNSUP                          # 8 B rows
+    assert _compact(L, kd=ctypes.c_void_p(4104)) == UNSUP            # misaligned
+    assert _compact(L, kd=Z, vd=Z, rows=0) == OK                     # nothing to write: no launch

@@ -382,3 +382,65 @@ def test_pipeline_workload3():
     ref_acc = oracle.tree_accept(ref_tree.parent, ref_tree.token, tgt, ref_tree.n_nodes)
     for g, e in zip(acc, ref_acc):
         assert np.array_equal(g.cpu().numpy(), e)
+
+
+# ----------------------------------------------------------------------------- KV compaction
+
+@pytest.mark.parametrize("dtype,D,Hkv", [("bf16", 128, 8), ("f32", 64, 2), ("bf16", 64, 1)])
+def test_kv_compact_after_accept(dtype, D, Hkv):
+    """tree_build -> tree_accept -> tree_kv_compact on the device against the oracle's
+    accept and compaction, bit for bit on the destination (written and untouched rows),
+    with one sequence's rows running past the end of the destination."""
+    rng = np.random.default_rng(900 + D + Hkv)
+    B, n_max = 7, 64
+    parent = np.full((B, n_max), -1, np.int32)
+    nn = rng.integers(1, n_max + 1, size=B).astype(np.int32)
+    nn[0], nn[1] = 1, 64
+    for b in range(B):
+        for i in range(1, int(nn[b])):
+            parent[b, i] = rng.integers(max(0, i - 3), i)                # deep, narrow trees
+    tok = rng.integers(0, 3, size=(B, n_max)).astype(np.int32)
+    tgt = rng.integers(0, 3, size=(B, n_max)).astype(np.int32)
+    parent[1, 1:] = np.arange(63)                                        # sequence 1: a chain whose
+    tgt[1, :63] = tok[1, 1:]                                             # every token passes
+    draw = (lambda s: synth.bf16_bits(rng.standard_normal(s).astype(np.float32))) if dtype == "bf16" \
+        else (lambda s: rng.standard_normal(s).astype(np.float32))
+    kt, vt = draw((B, n_max, Hkv, D)), draw((B, n_max, Hkv, D))
+    rows = 70 * B
+    kd, vd = draw((rows, Hkv, D)), draw((rows, Hkv, D))
+    dst = (np.arange(B) * 70).astype(np.int64)
+    dst[B - 1] = rows - 5                                                # only five rows fit
+
+    alen_r, best_r, _, path_r = oracle.tree_accept(parent, tok, tgt, nn)
+    kd_r, vd_r = oracle.kv_compact(kt, vt, path_r, alen_r, kd, vd, dst)
+
+    par_d, nn_d = dev_i32(parent), dev_i32(nn)
+    anc, depth, _, _ = tv.tree_build(par_d, nn_d)
+    alen, best, _, path = tv.tree_accept(par_d, depth, anc, nn_d, dev_i32(tok), dev_i32(tgt))
+    k_dst, v_dst = dev_input(kd, dtype), dev_input(vd, dtype)
+    tv.tree_kv_compact(dev_input(kt, dtype), dev_input(vt, dtype), path, alen, k_dst, v_dst,
+                       torch.from_numpy(dst).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(alen.cpu().numpy(), alen_r)
+    bits = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if dtype == "bf16" \
+        else (lambda t: t.cpu().numpy())
+    assert np.array_equal(bits(k_dst), kd_r)
+    assert np.array_equal(bits(v_dst), vd_r)
+    assert alen_r[1] == 63 and alen_r[0] == 0                            # whole chain; root only
+
+
+def test_kv_compact_rejected_tree_copies_nothing():
+    B, n_max, Hkv, D = 2, 64, 2, 64
+    kt = torch.randn((B, n_max, Hkv, D), device=DEV).to(torch.bfloat16)
+    vt = torch.randn((B, n_max, Hkv, D), device=DEV).to(torch.bfloat16)
+    kd = torch.zeros((100, Hkv, D), device=DEV, dtype=torch.bfloat16)
+    vd = torch.zeros((100, Hkv, D), device=DEV, dtype=torch.bfloat16)
+    path = torch.full((B, n_max), -1, dtype=torch.int32, device=DEV)
+    alen = torch.tensor([-1, 0], dtype=torch.int32, device=DEV)
+    dst = torch.tensor([0, 50], dtype=torch.int64, device=DEV)
+    tv.tree_kv_compact(kt, vt, path, alen, kd, vd, dst)
+    torch.cuda.synchronize()
+    written = torch.zeros(100, dtype=torch.bool)
+    written[50] = True
+    assert torch.equal(kd[50], kt[1, 0]) and torch.equal(vd[50], vt[1, 0])
+    assert torch.count_nonzero(kd[~written.to(DEV)]) == 0 and torch.count_nonzero(vd[~written.to(DEV)]) == 0

@@ -1,14 +1,16 @@
 """treeverify: EAGLE-style draft-tree verification on AMD MI355X (gfx950).
 
-The product is libtreeverify.so (C ABI in include/treeverify.h) with four calls --
-tree_build, tree_expand_rerank, tree_verify_attn, tree_accept -- and this thin
-binding that passes torch tensors' device pointers and torch's current stream to it.
+The product is libtreeverify.so (C ABI in include/treeverify.h) with the calls of
+the verification pass -- tree_build, tree_expand_rerank, tree_verify_attn,
+tree_accept -- plus tree_kv_compact (the accepted continuation into the KV cache),
+and this thin binding that passes torch tensors' device pointers and torch's current
+stream to it.
 """
 
 from ._lib import TreeVerifyError, lib, EXPORTS, LIB_PATH
 from .ops import (abi_version, tree_build, expand_workspace, ExpandOutputs, tree_expand_rerank,
-                  attn_workspace, tree_verify_attn, tree_accept)
+                  attn_workspace, tree_verify_attn, tree_accept, tree_kv_compact)
 
 __all__ = ["TreeVerifyError", "lib", "EXPORTS", "LIB_PATH", "abi_version", "tree_build",
            "expand_workspace", "ExpandOutputs", "tree_expand_rerank", "attn_workspace",
-           "tree_verify_attn", "tree_accept"]
+           "tree_verify_attn", "tree_accept", "tree_kv_compact"]

@@ -169,3 +169,26 @@ def tree_accept(parent, depth, anc, n_nodes, token, target_next, want_path=True)
                                            _ptr(alen), _ptr(best), _ptr(bonus), _ptr(path),
                                            _stream()))
     return alen, best, bonus, path
+
+
+def tree_kv_compact(k_tree, v_tree, path, accept_len, k_dst, v_dst, dst_row):
+    """Writes each sequence's accepted continuation (root, then the accepted path) from
+    the per-node K/V [B][n_max][Hkv][D] into rows dst_row[b] .. dst_row[b] + accept_len[b]
+    of k_dst / v_dst [rows][Hkv][D], in place."""
+    if k_tree.dtype not in _DT:
+        raise TypeError(f"k_tree must be float32 or bfloat16, got {k_tree.dtype}")
+    dt = k_tree.dtype
+    _need(k_tree, "k_tree", dt, 4)
+    B, n_max, Hkv, D = k_tree.shape
+    _need(v_tree, "v_tree", dt, shape=(B, n_max, Hkv, D))
+    _need(path, "path", torch.int32, shape=(B, n_max))
+    _need(accept_len, "accept_len", torch.int32, shape=(B,))
+    _need(k_dst, "k_dst", dt, 3)
+    if k_dst.shape[1:] != (Hkv, D):
+        raise ValueError(f"k_dst must be [rows][{Hkv}][{D}], got {tuple(k_dst.shape)}")
+    _need(v_dst, "v_dst", dt, shape=tuple(k_dst.shape))
+    _need(dst_row, "dst_row", torch.int64, shape=(B,))
+    check("tree_kv_compact", lib().tree_kv_compact(
+        _DT[dt], B, n_max, Hkv, D, _ptr(k_tree), _ptr(v_tree), _ptr(path), _ptr(accept_len),
+        _ptr(k_dst), _ptr(v_dst), _ptr(dst_row), int(k_dst.shape[0]), _stream()))
+    return k_dst, v_dst
