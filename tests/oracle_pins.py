@@ -577,6 +577,95 @@ def pin_compact_edges():
             np.array_equal(k2[38], kt[1, 1]) and np.array_equal(k2[39], kt[1, 2]))
 
 
+# ----------------------------------------------------------------------------- stochastic acceptance
+
+def _softmax_rows(rng, shape, scale=1.0):
+    x = rng.standard_normal(shape) * scale
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def pin_stochastic_greedy_limit(seed=51, trials=40):
+    """One-hot target distributions (at target_next[u]) and distinct sibling tokens:
+    for any uniforms the walk is greedy acceptance (checked against tree_accept)."""
+    rng = np.random.default_rng(seed)
+    V, n_max = 12, 16
+    for _ in range(trials):
+        n = int(rng.integers(1, n_max + 1))
+        parent = np.full((1, n_max), -1, np.int32)
+        tok = np.zeros((1, n_max), np.int32)
+        for i in range(1, n):
+            parent[0, i] = rng.integers(0, i)
+        for u in range(n):
+            kids = [c for c in range(1, n) if parent[0, c] == u]
+            tok[0, kids] = rng.choice(V, size=len(kids), replace=False)
+        tgt = rng.integers(0, V, size=(1, n_max)).astype(np.int32)
+        p = np.zeros((1, n_max, V), np.float32)
+        p[0, np.arange(n_max), tgt[0]] = 1.0
+        q = _softmax_rows(rng, (1, n_max, V))
+        ua = rng.random((1, n_max)).astype(np.float32)
+        ub = rng.random(1).astype(np.float32)
+        nn = np.array([n], np.int32)
+        a, bst, bon, path, ind = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+        ga, gb, gbon, gpath = oracle.tree_accept(parent, tok, tgt, nn)
+        if ind[0] or a[0] != ga[0] or bst[0] != gb[0] or bon[0] != gbon[0] or not np.array_equal(path, gpath):
+            return False
+    return True
+
+
+def pin_stochastic_hand_example():
+    """V = 4, root children with tokens 2 and 0, p = (0.1, 0.2, 0.3, 0.4), q = (0.25,
+    0.25, 0.5, 0).  Token 2 passes iff u < 0.3 / 0.5 = 0.6; after its rejection the
+    residual is (0, 0, 0, 0.4), token 0 then fails whatever u, and the bonus is token 3
+    whatever u; a passing token 2 moves to its leaf, whose bonus comes from its own
+    row: (0, 1, 0, 0) gives token 1."""
+    parent = np.array([[-1, 0, 0, -1]], np.int32)
+    tok = np.array([[9, 2, 0, 0]], np.int32)
+    nn = np.array([3], np.int32)
+    p = np.zeros((1, 4, 4), np.float32)
+    p[0, 0] = [0.1, 0.2, 0.3, 0.4]
+    p[0, 1] = [0.0, 1.0, 0.0, 0.0]
+    p[0, 2] = [1.0, 0.0, 0.0, 0.0]
+    q = np.zeros((1, 4, 4), np.float32)
+    q[0, 0] = [0.25, 0.25, 0.5, 0.0]
+    for u1, ub, want in [(0.7, 0.01, (0, 0, 3)), (0.7, 0.99, (0, 0, 3)), (0.59, 0.5, (1, 1, 1)),
+                         (0.0, 0.99, (1, 1, 1))]:
+        ua = np.array([[0.0, u1, 0.3, 0.0]], np.float32)
+        a, bst, bon, _, ind = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua,
+                                                            np.array([ub], np.float32))
+        if ind[0] or (int(a[0]), int(bst[0]), int(bon[0])) != want:
+            return False
+    return True
+
+
+def pin_stochastic_preserves_target(seed=52, trials=20000):
+    """Candidates drawn independently from the draft distribution: the first token the
+    walk emits (the passing child's token, else the bonus) follows the target's
+    distribution (rejection sampling leaves the output distribution unchanged)."""
+    rng = np.random.default_rng(seed)
+    V, k = 5, 3
+    p0 = np.array([0.05, 0.4, 0.15, 0.3, 0.1], np.float32)
+    q0 = np.array([0.3, 0.1, 0.3, 0.1, 0.2], np.float32)
+    parent = np.array([[-1] + [0] * k], np.int32)
+    nn = np.array([k + 1], np.int32)
+    p = np.zeros((1, k + 1, V), np.float32)
+    p[0, 0] = p0
+    p[0, 1:] = 1.0 / V
+    q = np.zeros((1, k + 1, V), np.float32)
+    q[0, 0] = q0
+    counts = np.zeros(V)
+    for _ in range(trials):
+        tok = np.zeros((1, k + 1), np.int32)
+        tok[0, 1:] = rng.choice(V, size=k, p=q0 / q0.sum())
+        ua = rng.random((1, k + 1)).astype(np.float32)
+        ub = rng.random(1).astype(np.float32)
+        a, bst, bon, _, _ = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+        counts[int(tok[0, bst[0]]) if a[0] == 1 else int(bon[0])] += 1
+    expect = trials * p0.astype(np.float64)
+    chi2 = float(np.sum((counts - expect) ** 2 / expect))
+    return chi2 < 20.0                       # 4 degrees of freedom: p-value ~ 5e-4
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -600,6 +689,9 @@ ALL_PINS = {
     "compact_root_only": pin_compact_root_only,
     "compact_root_path": pin_compact_root_path,
     "compact_edges": pin_compact_edges,
+    "stochastic_greedy_limit": pin_stochastic_greedy_limit,
+    "stochastic_hand_example": pin_stochastic_hand_example,
+    "stochastic_preserves_target": pin_stochastic_preserves_target,
 }
 
 

@@ -13,6 +13,7 @@ import oracle
 import oracle.accept
 import oracle.attention
 import oracle.compact
+import oracle.stochastic
 import oracle.expand
 import oracle.tree
 import oracle_pins
@@ -87,6 +88,14 @@ MUTATIONS = {
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [int(row[j]) for j in range(n)])],
     "compact: path kept leaf first": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n)][::-1])],
+    "stochastic: no residual after a rejection": [
+        (oracle.stochastic, "residual", lambda r, S, q: r.astype(np.float32))],
+    "stochastic: residual not clamped at zero": [
+        (oracle.stochastic, "residual", lambda r, S, q: r.astype(np.float32) - np.float32(S) * q.astype(np.float32))],
+    "stochastic: acceptance ratio inverted": [
+        (oracle.stochastic, "child_passes", lambda u, S, qx, rx: (float(u) * float(rx) < S * float(qx), 1.0))],
+    "stochastic: siblings tried last first": [
+        (oracle.stochastic, "children_of", lambda row, n, u: [c for c in range(n - 1, 0, -1) if int(row[c]) == u])],
     "compact: one node short": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }
