@@ -16,8 +16,9 @@ the tree_verify_attn call: its algorithmic bytes (prefix K/V + tree K/V + Q + O)
 divided by its average duration, measured with HIP events on its stream around
 graph replays of back-to-back attention calls over the rotated copies.  The CPU
 baseline is the plain oracle timed on a bounded sample on the host cores.  The KV
-compaction that follows acceptance (tree_kv_compact, outside the step) is timed the
-same way and reported beside the step.
+compaction that follows acceptance (tree_kv_compact) and the rejection-sampling
+acceptance (tree_accept_stochastic, on seeded target/draft distributions) are timed
+the same way, outside the step, and reported beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -284,9 +285,41 @@ def gpu_leg(args, inp):
     compact_ms = a0.elapsed_time(a1) / (args.attn_reps * R)
     el = 2 if w.dtype == "bf16" else 4
     compact_bytes = rows_written / R * w.Hkv * w.D * el * 2 * 2      # K and V, read and write
+
+    # stochastic (rejection-sampling) acceptance on the first copy's tree, with seeded
+    # target / draft distributions over the workload's vocabulary, when they fit
+    stoch = None
+    V = int(w.V)
+    if V <= 36864 and w.B * w.n_max * V * 8 <= (256 << 20):
+        rng = np.random.default_rng(77)
+        lq = rng.standard_normal((w.B, w.n_max, V), dtype=np.float32) * 2
+        lp = lq + rng.standard_normal((w.B, w.n_max, V), dtype=np.float32) * np.float32(0.7)
+        soft = lambda x: torch.softmax(torch.from_numpy(x).to(dev), dim=-1).contiguous()
+        p_t, q_d = soft(lp), soft(lq)
+        ua = torch.from_numpy(rng.random((w.B, w.n_max), dtype=np.float32)).to(dev)
+        ub = torch.from_numpy(rng.random(w.B, dtype=np.float32)).to(dev)
+        par, nn, tok = tree_of(copies[0])
+        anc, _, _, _ = tv.tree_build(par, nn, prefix_len)
+        run_s = lambda: tv.tree_accept_stochastic(par, anc, nn, tok, p_t, q_d, ua, ub)
+        with torch.cuda.stream(side):
+            run_s()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            s_keep = [run_s() for _ in range(4)]
+        sg.replay()
+        torch.cuda.synchronize()
+        a0.record(stream)
+        for _ in range(args.attn_reps):
+            sg.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        stoch = {"us_per_call": a0.elapsed_time(a1) / (args.attn_reps * 4) * 1e3, "vocab": V,
+                 "accepted_per_seq": float(s_keep[0][0].float().mean().item())}
     return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, copies=R,
                 tree=tree_host, compact_ms=compact_ms, compact_bytes=compact_bytes,
-                compact_rows=rows_written / R)
+                compact_rows=rows_written / R, stochastic=stoch)
 
 
 def copy_reference(mib):
@@ -396,6 +429,8 @@ def main():
                        "bytes_per_call": g["compact_bytes"],
                        "GB/s": g["compact_bytes"] / (g["compact_ms"] * 1e-3) / 1e9},
     }
+    if g["stochastic"] is not None:
+        line["accept_stochastic"] = g["stochastic"]
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_leg(args, inp, g["tree"])
     print(json.dumps(line), flush=True)

@@ -194,6 +194,43 @@ tv_status tree_accept(int B, int n_max, const int32_t* parent, const int32_t* de
                       int32_t* bonus_token, int32_t* path, hipStream_t stream);
 
 /*
+ * tree_accept_stochastic -- rejection-sampling acceptance over the tree.
+ * [EAGLE] "Well-Calibrated Draft Model": under random sampling a draft token x is
+ * accepted with rate min(1, P_target(x) / P_draft(x)).  [EAGLE-3] section 4 steps 3-4:
+ * a rejected token gives way to the target's own token, sampled from a corrected
+ * distribution; the longest passing prefix of the tree is kept.  [EAGLE-4]
+ * "verification trees and the harness": rejection sampling leaves the output
+ * distribution unchanged.  The pages give the one-candidate rule only; for a tree:
+ * from the root, the current node u's children are tried in index order.  With r
+ * the target weights (p_target[u] at first) and S their float64 sum, child c with
+ * token x passes when u_accept[c] * S * q_draft[u][x] < r[x] (float64, left to right;
+ * with q == 0: when r[x] > 0) and becomes the current node; a failing child turns r
+ * into max(r - fl32(S) * q_draft[u], 0) (float32 product, then difference).  When
+ * no child passes, the bonus token is the first v whose float64 running sum of r
+ * exceeds u_bonus * S (the last v with r > 0 if rounding leaves none).
+ *
+ *   parent, anc, n_nodes, token  as for tree_accept (a tree tree_build accepted)
+ *   p_target   float32 [B][n_max][vocab]  target's next-token distribution after
+ *                                        node i's root path
+ *   q_draft    float32 [B][n_max][vocab]  draft's distribution that proposed node
+ *                                        i's children
+ *   u_accept   float32 [B][n_max]  uniform in [0,1) used when node i is a candidate
+ *   u_bonus    float32 [B]         uniform in [0,1) for the bonus token
+ *   accept_len, best_node, bonus_token int32 [B], path int32 [B][n_max] (nullable):
+ *                 as for tree_accept
+ * 1 <= vocab <= 36864 (else TV_ERR_UNSUPPORTED; the weights live in LDS).  Tokens
+ * outside [0, vocab) fail.
+ * Sums in float64 depend on their order in the last bits: a decision within ~1e-15
+ * (relative) of its threshold may differ from a sequential evaluation.
+ */
+tv_status tree_accept_stochastic(int B, int n_max, int vocab, const int32_t* parent,
+                                 const uint64_t* anc, const int32_t* n_nodes,
+                                 const int32_t* token, const float* p_target,
+                                 const float* q_draft, const float* u_accept,
+                                 const float* u_bonus, int32_t* accept_len, int32_t* best_node,
+                                 int32_t* bonus_token, int32_t* path, hipStream_t stream);
+
+/*
  * tree_kv_compact -- the accepted continuation's K/V into the KV cache.
  * [EAGLE-4] "verification trees and the harness": after verification the harness
  * keeps the accepted continuation, frees the rejected KV-cache entries and starts

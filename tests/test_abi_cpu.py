@@ -169,3 +169,15 @@ def test_kv_compact_validation(L):
     assert _compact(L, Hkv=1, D=4) == UNSUP                          # 8 B rows
     assert _compact(L, kd=ctypes.c_void_p(4104)) == UNSUP            # misaligned
     assert _compact(L, kd=Z, vd=Z, rows=0) == OK                     # nothing to write: no launch
+
+
+def _stoch(L, B=2, n_max=64, V=1000, p=P):
+    return L.tree_accept_stochastic(B, n_max, V, P, P, P, P, p, P, P, P, P, P, P, Z, Z)
+
+
+def test_accept_stochastic_validation(L):
+    assert _stoch(L, p=Z) == NULL
+    assert _stoch(L, B=0) == SHAPE
+    assert _stoch(L, n_max=65) == SHAPE
+    assert _stoch(L, V=0) == SHAPE
+    assert _stoch(L, V=36865) == UNSUP

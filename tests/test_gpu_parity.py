@@ -444,3 +444,86 @@ def test_kv_compact_rejected_tree_copies_nothing():
     written[50] = True
     assert torch.equal(kd[50], kt[1, 0]) and torch.equal(vd[50], vt[1, 0])
     assert torch.count_nonzero(kd[~written.to(DEV)]) == 0 and torch.count_nonzero(vd[~written.to(DEV)]) == 0
+
+
+# ----------------------------------------------------------------------------- stochastic acceptance
+
+def _stochastic_case(seed, B, V, n_max=64, scale=2.0, one_hot=False):
+    """Random trees whose children's tokens are drawn (without repeats) from the draft
+    distribution of their parent; target rows close to the draft rows, so that about
+    half of the candidates pass."""
+    rng = np.random.default_rng(seed)
+    parent = np.full((B, n_max), -1, np.int32)
+    nn = rng.integers(1, n_max + 1, size=B).astype(np.int32)
+    for b in range(B):
+        for i in range(1, int(nn[b])):
+            parent[b, i] = rng.integers(max(0, i - 6), i)
+    lq = rng.standard_normal((B, n_max, V)) * scale
+    lp = lq + rng.standard_normal((B, n_max, V)) * 0.7
+    sm = lambda x: (np.exp(x - x.max(-1, keepdims=True)) / np.exp(x - x.max(-1, keepdims=True)).sum(-1, keepdims=True))
+    q = sm(lq).astype(np.float32)
+    p = sm(lp).astype(np.float32)
+    tgt = rng.integers(0, V, size=(B, n_max)).astype(np.int32)
+    if one_hot:
+        p = np.zeros_like(p)
+        p[np.arange(B)[:, None], np.arange(n_max)[None, :], tgt] = 1.0
+    tok = np.zeros((B, n_max), np.int32)
+    for b in range(B):
+        for u in range(int(nn[b])):
+            kids = [c for c in range(1, int(nn[b])) if parent[b, c] == u]
+            if kids:
+                w = q[b, u].astype(np.float64)
+                tok[b, kids] = rng.choice(V, size=len(kids), replace=False, p=w / w.sum())
+        if one_hot:                        # make some children match the target
+            for c in range(1, int(nn[b])):
+                if rng.random() < 0.6:
+                    sib = [s for s in range(1, int(nn[b])) if parent[b, s] == parent[b, c] and s != c]
+                    if tgt[b, parent[b, c]] not in tok[b, sib]:
+                        tok[b, c] = tgt[b, parent[b, c]]
+    ua = rng.random((B, n_max)).astype(np.float32)
+    ub = rng.random(B).astype(np.float32)
+    return parent, nn, tok, tgt, p, q, ua, ub
+
+
+def _run_stochastic(parent, nn, tok, p, q, ua, ub):
+    par_d, nn_d = dev_i32(parent), dev_i32(nn)
+    anc, _, _, _ = tv.tree_build(par_d, nn_d)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    out = tv.tree_accept_stochastic(par_d, anc, nn_d, dev_i32(tok), f(p), f(q), f(ua), f(ub))
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("seed,B,V", [(1, 6, 1000), (2, 4, 5000), (3, 2, 32000), (4, 8, 37)])
+def test_accept_stochastic_matches_oracle(seed, B, V):
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V)
+    alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    ok = ~indet
+    assert ok.sum() >= B - 1
+    assert np.array_equal(alen[ok], alen_r[ok])
+    assert np.array_equal(best[ok], best_r[ok])
+    assert np.array_equal(bonus[ok], bonus_r[ok])
+    assert np.array_equal(path[ok], path_r[ok])
+    assert alen_r.max() >= 1                                         # some candidates passed
+
+
+def test_accept_stochastic_greedy_limit_equals_tree_accept():
+    """One-hot target rows: the device's stochastic walk equals its greedy acceptance."""
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(9, 6, 300, one_hot=True)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    par_d, nn_d = dev_i32(parent), dev_i32(nn)
+    anc, depth, _, _ = tv.tree_build(par_d, nn_d)
+    g = [t.cpu().numpy() for t in tv.tree_accept(par_d, depth, anc, nn_d, dev_i32(tok), dev_i32(tgt))]
+    assert np.array_equal(alen, g[0]) and np.array_equal(best, g[1])
+    assert np.array_equal(bonus, g[2]) and np.array_equal(path, g[3])
+    assert g[0].max() >= 2
+
+
+def test_accept_stochastic_invalid_tree():
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(10, 3, 64)
+    parent[1, 5] = 7                                                 # a forward link: rejected
+    nn[2] = 0
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    for b in (1, 2):
+        assert alen[b] == -1 and best[b] == -1 and bonus[b] == -1 and np.all(path[b] == -1)

@@ -12,7 +12,7 @@ TV_F32, TV_BF16 = 0, 1
 
 EXPORTS = ("tv_abi_version", "tv_status_string", "tree_build", "tree_expand_workspace_size",
            "tree_expand_rerank", "tree_verify_attn_workspace_size", "tree_verify_attn",
-           "tree_accept", "tree_kv_compact")
+           "tree_accept", "tree_accept_stochastic", "tree_kv_compact")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -30,6 +30,8 @@ _SIGNATURES = {
     "tree_verify_attn": (_I, [_I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _P, _P, _S, _P, _P]),
     "tree_accept": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "tree_accept_stochastic": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P]),
     "tree_kv_compact": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
 }
 

@@ -192,3 +192,30 @@ def tree_kv_compact(k_tree, v_tree, path, accept_len, k_dst, v_dst, dst_row):
         _DT[dt], B, n_max, Hkv, D, _ptr(k_tree), _ptr(v_tree), _ptr(path), _ptr(accept_len),
         _ptr(k_dst), _ptr(v_dst), _ptr(dst_row), int(k_dst.shape[0]), _stream()))
     return k_dst, v_dst
+
+
+def tree_accept_stochastic(parent, anc, n_nodes, token, p_target, q_draft, u_accept, u_bonus,
+                           want_path=True):
+    """(accept_len, best_node, bonus_token, path): rejection-sampling acceptance.
+    p_target, q_draft float32 [B][n_max][vocab]; u_accept [B][n_max], u_bonus [B]."""
+    _need(parent, "parent", torch.int32, 2)
+    B, n_max = parent.shape
+    _need(anc, "anc", torch.int64, shape=(B, n_max))
+    _need(n_nodes, "n_nodes", torch.int32, shape=(B,))
+    _need(token, "token", torch.int32, shape=(B, n_max))
+    _need(p_target, "p_target", torch.float32, 3)
+    V = p_target.shape[2]
+    _need(p_target, "p_target", torch.float32, shape=(B, n_max, V))
+    _need(q_draft, "q_draft", torch.float32, shape=(B, n_max, V))
+    _need(u_accept, "u_accept", torch.float32, shape=(B, n_max))
+    _need(u_bonus, "u_bonus", torch.float32, shape=(B,))
+    dev = parent.device
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    best = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    path = torch.empty((B, n_max), dtype=torch.int32, device=dev) if want_path else None
+    check("tree_accept_stochastic", lib().tree_accept_stochastic(
+        B, n_max, V, _ptr(parent), _ptr(anc), _ptr(n_nodes), _ptr(token), _ptr(p_target),
+        _ptr(q_draft), _ptr(u_accept), _ptr(u_bonus), _ptr(alen), _ptr(best), _ptr(bonus),
+        _ptr(path), _stream()))
+    return alen, best, bonus, path
