@@ -75,7 +75,22 @@ def row_topk(row, k):
     return np.argsort(-row, kind="stable")[:k]
 
 
-def expand_rerank(logits_steps, k, m, root_token, n_max=64):
+def budget_cut(ranked_scores, budget_log):
+    """Candidates kept by the verify budget: the leading run of the best-first ranked
+    candidates whose score (log value) exceeds the bar for their place: candidate j
+    (1-based) passes when score_j > budget_log[j] (float32), and the first failure
+    ends the run.  "Technical analysis of EAGLE-4", section "EAGLE-4 verification
+    trees and the harness": candidates are added while the gain in cumulative
+    probability per unit of measured verification cost stays above a threshold."""
+    n = 0
+    for j, sc in enumerate(ranked_scores, start=1):
+        if not np.float32(sc) > np.float32(budget_log[j]):
+            break
+        n = j
+    return n
+
+
+def expand_rerank(logits_steps, k, m, root_token, n_max=64, budget_log=None):
     """Build each sequence's dynamic draft tree level by level, then rerank it.
 
     logits_steps  list of S float32 arrays; level s (1-based) has shape
@@ -83,6 +98,8 @@ def expand_rerank(logits_steps, k, m, root_token, n_max=64):
     k             children per expanded node and frontier width.
     m             nodes kept including the root: int, or int array [B].
     root_token    int [B], the token of each root.
+    budget_log    optional float32 [n_max]: after the best m-1 are chosen, only the
+                  leading run passing budget_cut is kept.
     """
     S = len(logits_steps)
     B = logits_steps[0].shape[0]
@@ -132,6 +149,8 @@ def expand_rerank(logits_steps, k, m, root_token, n_max=64):
             continue
         order = sorted(range(len(pool)), key=lambda i: rank_key(pool[i][2], i))
         kept = order[:mb - 1]
+        if budget_log is not None:
+            kept = kept[:budget_cut([pool[i][2] for i in kept], budget_log)]
         kept.sort(key=lambda i: (pool[i][3], i))
         where = {i: j + 1 for j, i in enumerate(kept)}
         parent[b, 0] = -1

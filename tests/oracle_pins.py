@@ -666,6 +666,54 @@ def pin_stochastic_preserves_target(seed=52, trials=20000):
     return chi2 < 20.0                       # 4 degrees of freedom: p-value ~ 5e-4
 
 
+# ----------------------------------------------------------------------------- verify budget
+
+def _budget_case(seed=61):
+    rng = np.random.default_rng(seed)
+    B, k, S, V = 3, 4, 4, 50
+    steps = [(rng.standard_normal((B, 1 if s == 0 else k, V)) * 2).astype(np.float32) for s in range(S)]
+    return steps, k, rng.integers(0, V, size=B)
+
+
+def pin_budget_limits():
+    """A bar of -inf keeps what the plain rerank keeps; +inf keeps the root only; a
+    bar just under the j-th best score keeps exactly j candidates."""
+    steps, k, roots = _budget_case()
+    plain = oracle.expand_rerank(steps, k, 20, roots)
+    lo = oracle.expand_rerank(steps, k, 20, roots, budget_log=np.full(64, -np.inf, np.float32))
+    hi = oracle.expand_rerank(steps, k, 20, roots, budget_log=np.full(64, np.inf, np.float32))
+    if not (np.array_equal(plain.parent, lo.parent) and np.array_equal(plain.n_nodes, lo.n_nodes)):
+        return False
+    if not np.all(hi.n_nodes == 1):
+        return False
+    for b in range(3):
+        sc = np.sort(plain.score[b, 1:plain.n_nodes[b]])[::-1]       # best first
+        for j in (1, 5, 11):
+            bar = np.full(64, -np.inf, np.float32)
+            bar[j + 1:] = sc[j]                                       # candidate j+1 ties the bar
+            cut = oracle.expand_rerank(steps, k, 20, roots, budget_log=bar)
+            if cut.n_nodes[b] != j + 1:
+                return False
+            # the kept nodes are exactly the plain tree's j best, ancestors included
+            kept = np.sort(cut.score[b, 1:j + 1])[::-1]
+            if not np.array_equal(kept, sc[:j]):
+                return False
+            par = cut.parent[b, 1:j + 1]
+            if not np.all((par >= 0) & (par < np.arange(1, j + 1))):
+                return False
+    return True
+
+
+def pin_budget_first_failure_stops():
+    """A bar that only the 3rd candidate fails keeps two, though later ones pass."""
+    steps, k, roots = _budget_case(62)
+    plain = oracle.expand_rerank(steps, k, 12, roots)
+    bar = np.full(64, -np.inf, np.float32)
+    bar[3] = np.inf
+    cut = oracle.expand_rerank(steps, k, 12, roots, budget_log=bar)
+    return bool(np.all(cut.n_nodes == 3)) and bool(np.all(plain.n_nodes == 12))
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -692,6 +740,8 @@ ALL_PINS = {
     "stochastic_greedy_limit": pin_stochastic_greedy_limit,
     "stochastic_hand_example": pin_stochastic_hand_example,
     "stochastic_preserves_target": pin_stochastic_preserves_target,
+    "budget_limits": pin_budget_limits,
+    "budget_first_failure_stops": pin_budget_first_failure_stops,
 }
 
 

@@ -96,6 +96,10 @@ MUTATIONS = {
         (oracle.stochastic, "child_passes", lambda u, S, qx, rx: (float(u) * float(rx) < S * float(qx), 1.0))],
     "stochastic: siblings tried last first": [
         (oracle.stochastic, "children_of", lambda row, n, u: [c for c in range(n - 1, 0, -1) if int(row[c]) == u])],
+    "budget: counts every passing candidate": [
+        (oracle.expand, "budget_cut", lambda sc, bl: sum(1 for j, x in enumerate(sc, 1) if np.float32(x) > bl[j]))],
+    "budget: a tie passes": [
+        (oracle.expand, "budget_cut", lambda sc, bl: next((j - 1 for j, x in enumerate(sc, 1) if not np.float32(x) >= bl[j]), len(sc)))],
     "compact: one node short": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }
