@@ -116,6 +116,13 @@ tv_status tree_build(int B, int n_max, const int32_t* parent, const int32_t* n_n
  * creation), with parents remapped to output indices:
  *   parent int32 [B][n_max], token int32 [B][n_max] (token[b][0] = root_token[b]),
  *   score fp32 [B][n_max] (root 0), n_nodes int32 [B]; padding -1 / -1 / 0.
+ * budget_log float32 [64] (device, nullable; last level only) is a verify budget
+ * ([EAGLE-4] "verification trees and the harness": candidates are added while the
+ * gain in cumulative probability per unit of measured verification cost stays above
+ * a threshold): of the m - 1 kept, best first, candidate j (1-based) stays when its
+ * score exceeds budget_log[j], and the first one that does not ends the run (the
+ * kept set stays ancestor-closed).  tree_budget_thresholds derives it from a cost
+ * table.
  * frontier_token int32 [B][k] (nullable) receives the tokens of the new frontier by
  * rank at every step, for the caller's next draft pass.
  * Limits: 1 <= k <= 16, k <= vocab <= 1048576, max_steps >= 1, k + (max_steps-1)*k*k <= 4096,
@@ -126,9 +133,26 @@ tv_status tree_build(int B, int n_max, const int32_t* parent, const int32_t* n_n
 size_t tree_expand_workspace_size(int B, int k, int max_steps);
 tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int max_steps, int step,
                              int vocab, const float* logits, int final_m, const int32_t* m_per_seq,
-                             const int32_t* root_token, int n_max, int32_t* parent, int32_t* token,
-                             float* score, int32_t* n_nodes, int32_t* frontier_token,
-                             int32_t* seq_status, hipStream_t stream);
+                             const float* budget_log, const int32_t* root_token, int n_max,
+                             int32_t* parent, int32_t* token, float* score, int32_t* n_nodes,
+                             int32_t* frontier_token, int32_t* seq_status, hipStream_t stream);
+
+/*
+ * tree_budget_thresholds -- the per-place bars of the verify budget (HOST pointers,
+ * no device work).  [EAGLE-4] "verification trees and the harness": a calibrated cost
+ * table (verification latency against batch, context length and candidate count)
+ * and a threshold on the gain in cumulative probability per marginal cost.  A
+ * candidate's value is exp(score), the product of the confidences on its path.
+ *   cost_us    [n_max] host: latency of one tree_verify_attn call with N = 1..n_max
+ *              nodes per tree (cost_us[N-1]) at the caller's batch and context length
+ *   threshold  accepted tokens per microsecond a candidate must bring
+ *   budget_log [64] host out: budget_log[j] = log(threshold * (cost_us[j] -
+ *              cost_us[j-1])) for 1 <= j < n_max (candidate j makes the tree j + 1
+ *              nodes); -inf where that marginal cost is <= 0 or threshold <= 0, and for
+ *              j = 0 and j >= n_max
+ */
+tv_status tree_budget_thresholds(const float* cost_us, int n_max, float threshold,
+                                 float* budget_log);
 
 /*
  * tree_verify_attn -- tree-masked attention of one target layer over all draft nodes.

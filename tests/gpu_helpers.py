@@ -66,7 +66,7 @@ def attn_close(got, ref, what=""):
     return ok, f"{what} max_abs={err:.3e} max_ref={scale:.3e}"
 
 
-def run_expand(levels, k, m, root_token, n_max=64, m_per_seq=None):
+def run_expand(levels, k, m, root_token, n_max=64, m_per_seq=None, budget_log=None):
     """All levels of tree_expand_rerank on the device; returns the outputs and the
     frontier tokens after each level."""
     B = levels[0].shape[0]
@@ -75,12 +75,13 @@ def run_expand(levels, k, m, root_token, n_max=64, m_per_seq=None):
     out = tv.ExpandOutputs(B, n_max, k, DEV)
     roots = dev_i32(root_token)
     mps = None if m_per_seq is None else dev_i32(m_per_seq)
+    bud = None if budget_log is None else dev_f32(budget_log)
     fronts = []
     for s in range(S):
         lg = dev_f32(levels[s])
         final = (m if np.isscalar(m) else 64) if s == S - 1 else 0
         tv.tree_expand_rerank(ws, s + 1, lg, k, S, final_m=int(final), m_per_seq=mps,
-                              root_token=roots, n_max=n_max, out=out)
+                              root_token=roots, n_max=n_max, out=out, budget_log=bud)
         fronts.append(out.frontier_token.cpu().numpy().copy())
     torch.cuda.synchronize()
     return out, fronts

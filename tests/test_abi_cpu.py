@@ -62,7 +62,7 @@ def test_tree_accept_validation(L):
 def _expand(L, ws=P, ws_bytes=1 << 30, B=2, k=4, max_steps=3, step=1, vocab=100, logits=P,
             final_m=0, root=Z, n_max=64, parent=Z, token=Z, score=Z, n_nodes=Z):
     return L.tree_expand_rerank(ws, ws_bytes, B, k, max_steps, step, vocab, logits, final_m, Z,
-                                root, n_max, parent, token, score, n_nodes, Z, Z, Z)
+                                Z, root, n_max, parent, token, score, n_nodes, Z, Z, Z)
 
 
 def test_expand_validation(L):
@@ -181,3 +181,17 @@ def test_accept_stochastic_validation(L):
     assert _stoch(L, n_max=65) == SHAPE
     assert _stoch(L, V=0) == SHAPE
     assert _stoch(L, V=36865) == UNSUP
+
+
+def test_budget_thresholds(L):
+    import numpy as np
+    out = np.empty(64, np.float32)
+    cost = np.array([10, 10, 11, 13, 12, 20], np.float32)           # N = 1..6 nodes
+    assert L.tree_budget_thresholds(cost.ctypes.data, 6, 0.5, out.ctypes.data) == OK
+    assert np.isneginf(out[0]) and np.isneginf(out[1]) and np.isneginf(out[4])   # free, cheaper
+    assert out[2] == np.float32(np.log(0.5 * 1.0)) and out[3] == np.float32(np.log(0.5 * 2.0))
+    assert out[5] == np.float32(np.log(0.5 * 8.0)) and np.all(np.isneginf(out[6:]))
+    assert L.tree_budget_thresholds(cost.ctypes.data, 6, 0.0, out.ctypes.data) == OK
+    assert np.all(np.isneginf(out))
+    assert L.tree_budget_thresholds(Z, 6, 0.5, out.ctypes.data) == NULL
+    assert L.tree_budget_thresholds(cost.ctypes.data, 65, 0.5, out.ctypes.data) == SHAPE

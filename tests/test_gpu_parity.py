@@ -109,9 +109,10 @@ def test_accept_full_chain_and_no_match():
 
 # ----------------------------------------------------------------------------- expansion
 
-def _check_expand(levels, k, m, roots, m_per_seq=None):
-    ref = oracle.expand_rerank(levels, k, m if m_per_seq is None else m_per_seq, roots)
-    out, fronts = run_expand(levels, k, m, roots, m_per_seq=m_per_seq)
+def _check_expand(levels, k, m, roots, m_per_seq=None, budget_log=None):
+    ref = oracle.expand_rerank(levels, k, m if m_per_seq is None else m_per_seq, roots,
+                               budget_log=budget_log)
+    out, fronts = run_expand(levels, k, m, roots, m_per_seq=m_per_seq, budget_log=budget_log)
     st = out.seq_status.cpu().numpy()
     assert np.array_equal(st, ref.status)
     n = out.n_nodes.cpu().numpy()
@@ -527,3 +528,31 @@ def test_accept_stochastic_invalid_tree():
     alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
     for b in (1, 2):
         assert alen[b] == -1 and best[b] == -1 and bonus[b] == -1 and np.all(path[b] == -1)
+
+
+
+# ----------------------------------------------------------------------------- verify budget
+
+@pytest.mark.parametrize("wid", [3, 5])
+def test_expand_verify_budget(wid):
+    """The final rerank under a verify budget derived from a cost table that grows past
+    16 nodes: bit-exact against the oracle, and narrower trees than without it."""
+    w = synth.WORKLOADS[wid]
+    cost = np.concatenate([np.full(16, 20.0), 20.0 + 0.5 * np.arange(1, 49)]).astype(np.float32)
+    bar = tv.budget_thresholds(cost, 1e-4)
+    kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+    ref = _check_expand(synth.draft_logits(w), w.k, w.m if kc is None else 64, synth.root_tokens(w),
+                        m_per_seq=kc, budget_log=bar)
+    plain = oracle.expand_rerank(synth.draft_logits(w), w.k, w.m if kc is None else kc,
+                                 synth.root_tokens(w))
+    assert np.all(ref.n_nodes <= plain.n_nodes) and np.any(ref.n_nodes < plain.n_nodes)
+    assert np.all(ref.n_nodes >= np.minimum(plain.n_nodes, 16))
+
+
+def test_expand_budget_limits_on_device():
+    rng = np.random.default_rng(71)
+    levels = [(rng.standard_normal((2, 1 if s == 0 else 6, 500)) * 2).astype(np.float32) for s in range(4)]
+    roots = rng.integers(0, 500, size=2)
+    for bar in (np.full(64, -np.inf, np.float32), np.full(64, np.inf, np.float32)):
+        ref = _check_expand(levels, 6, 40, roots, budget_log=bar)
+        assert np.all(ref.n_nodes == (40 if bar[1] < 0 else 1))

@@ -308,8 +308,9 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
 
 __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     char* __restrict__ ws, size_t stride, size_t rec_off, int k, int step, int rows, int nch,
-    int final_m, const int32_t* __restrict__ m_per_seq, const int32_t* __restrict__ root_token,
-    int n_max, int32_t* __restrict__ parent, int32_t* __restrict__ token,
+    int final_m, const int32_t* __restrict__ m_per_seq, const float* __restrict__ budget_log,
+    const int32_t* __restrict__ root_token, int n_max, int32_t* __restrict__ parent,
+    int32_t* __restrict__ token,
     float* __restrict__ score, int32_t* __restrict__ n_nodes, int32_t* __restrict__ frontier_token,
     int32_t* __restrict__ seq_status) {
   const int b = blockIdx.x;
@@ -332,7 +333,8 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   __shared__ int s_front[kTopKMax];
   __shared__ int s_kept[TV_MAX_NODES];
   __shared__ int s_kdep[TV_MAX_NODES];
-  __shared__ int s_nkept;
+  __shared__ int s_byrank[TV_MAX_NODES];
+  __shared__ int s_nkept, s_cut;
   __shared__ int s_status;
   __shared__ int s_m;
   __shared__ int s_rowbad;
@@ -539,6 +541,28 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
         }
         __syncthreads();
       }
+      // verify budget: rank the kept entries best first (score, then creation); the
+      // leading run of places j whose score exceeds budget_log[j] stays
+      if (budget_log && keep > 0) {
+        if (tid == 0) s_cut = keep;
+        __syncthreads();
+        if (tid < keep) {
+          const int me = s_kept[tid];
+          const uint32_t km = s_key[me];
+          int r = 0;
+          for (int o = 0; o < keep; ++o) {
+            const int other = s_kept[o];
+            const uint32_t ko = s_key[other];
+            r += (ko > km) || (ko == km && other < me);
+          }
+          s_byrank[r] = me;
+          if (!(pool[me].score > budget_log[r + 1])) atomicMin(&s_cut, r);
+        }
+        __syncthreads();
+        keep = s_cut;
+        if (tid < keep) s_kept[tid] = s_byrank[tid];
+        __syncthreads();
+      }
       if (tid < keep) s_kdep[tid] = s_dep[s_kept[tid]];
       __syncthreads();
       // output position: root first, then by (depth, creation)
@@ -633,7 +657,8 @@ TV_API size_t tree_expand_workspace_size(int B, int k, int max_steps) {
 
 TV_API tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int max_steps,
                                     int step, int vocab, const float* logits, int final_m,
-                                    const int32_t* m_per_seq, const int32_t* root_token, int n_max,
+                                    const int32_t* m_per_seq, const float* budget_log,
+                                    const int32_t* root_token, int n_max,
                                     int32_t* parent, int32_t* token, float* score,
                                     int32_t* n_nodes, int32_t* frontier_token, int32_t* seq_status,
                                     hipStream_t stream) {
@@ -663,6 +688,21 @@ TV_API tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int
   if (s != TV_OK) return s;
   hipLaunchKernelGGL(tv::expand_select_kernel, dim3(B), dim3(tv::kSelThreads), 0, stream,
                      (char*)ws, stride, rec_off, k, step, rows, rp.nch, final_m, m_per_seq,
-                     root_token, n_max, parent, token, score, n_nodes, frontier_token, seq_status);
+                     budget_log, root_token, n_max, parent, token, score, n_nodes, frontier_token,
+                     seq_status);
   return tv::launch_status();
+}
+
+TV_API tv_status tree_budget_thresholds(const float* cost_us, int n_max, float threshold,
+                                        float* budget_log) {
+  if (!cost_us || !budget_log) return TV_ERR_NULL;
+  if (n_max < 1 || n_max > TV_MAX_NODES) return TV_ERR_SHAPE;
+  for (int j = 0; j < TV_MAX_NODES; ++j) budget_log[j] = -INFINITY;
+  for (int j = 1; j < n_max; ++j) {
+    // candidate j brings the tree from j to j + 1 nodes
+    const double marginal = (double)cost_us[j] - (double)cost_us[j - 1];
+    if (threshold > 0.f && marginal > 0.0)
+      budget_log[j] = (float)log((double)threshold * marginal);
+  }
+  return TV_OK;
 }

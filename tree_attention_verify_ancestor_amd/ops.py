@@ -82,8 +82,9 @@ class ExpandOutputs:
 
 
 def tree_expand_rerank(ws, step, logits, k, max_steps, final_m=0, m_per_seq=None,
-                       root_token=None, n_max=64, out=None):
-    """One EAGLE-2 level.  logits: fp32 [B][1 if step == 1 else k][vocab]."""
+                       root_token=None, n_max=64, out=None, budget_log=None):
+    """One EAGLE-2 level.  logits: fp32 [B][1 if step == 1 else k][vocab].  budget_log:
+    optional fp32 [64] device tensor of per-place bars (see budget_thresholds)."""
     _need(ws, "ws", torch.uint8, 1)
     _need(logits, "logits", torch.float32, 3)
     B, rows, vocab = logits.shape
@@ -93,13 +94,27 @@ def tree_expand_rerank(ws, step, logits, k, max_steps, final_m=0, m_per_seq=None
         _need(m_per_seq, "m_per_seq", torch.int32, shape=(B,))
     if root_token is not None:
         _need(root_token, "root_token", torch.int32, shape=(B,))
+    if budget_log is not None:
+        _need(budget_log, "budget_log", torch.float32, shape=(64,))
     if out is None:
         out = ExpandOutputs(B, n_max, k, logits.device)
     check("tree_expand_rerank", lib().tree_expand_rerank(
         _ptr(ws), ws.numel(), B, k, max_steps, step, vocab, _ptr(logits), final_m,
-        _ptr(m_per_seq), _ptr(root_token), n_max, _ptr(out.parent), _ptr(out.token),
+        _ptr(m_per_seq), _ptr(budget_log), _ptr(root_token), n_max, _ptr(out.parent), _ptr(out.token),
         _ptr(out.score), _ptr(out.n_nodes), _ptr(out.frontier_token), _ptr(out.seq_status),
         _stream()))
+    return out
+
+
+def budget_thresholds(cost_us, threshold):
+    """Per-place bars of the verify budget from a cost table: cost_us[N-1] = latency of
+    one tree_verify_attn call with N nodes per tree (N = 1..n_max).  Returns a host
+    float32 array [64] (computed by the library's host helper)."""
+    import numpy as np
+    c = np.ascontiguousarray(cost_us, dtype=np.float32)
+    out = np.empty(64, dtype=np.float32)
+    check("tree_budget_thresholds", lib().tree_budget_thresholds(
+        c.ctypes.data, int(c.shape[0]), float(threshold), out.ctypes.data))
     return out
 
 
