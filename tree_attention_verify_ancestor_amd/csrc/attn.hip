@@ -579,6 +579,16 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       }
     };
 
+    // a full prefix stage: no mask, every subtile present, a fixed number of row tiles
+    auto stage_full = [&](auto ntile_tag, int st) {
+      const char* kb = smem + k_tile(st);
+      const char* vb = kb + v_tile(st);
+      const int kbase = stage_kbase(st);
+#pragma unroll
+      for (int j = 0; j < NSW; ++j)
+        subtile_fast(ic<kFull>{}, ntile_tag, kb, vb, wk + j * WK, kbase, c1, false);
+    };
+
     // ---- pipeline over the stages: the tree stage and up to NBUF prefix stages in
     // flight.  Q and the bitsets were loaded before the first stage's DMAs; one wait
     // for all of them (stage 0 is needed first in any case) also tells the compiler
@@ -593,7 +603,26 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
     if (!wave_live) {
       for (int st = 0; st < nst; ++st) begin_stage(st);
     } else {
-      for (int st = 0; st < nst; ++st) {
+      // The tree stage and a partial last prefix stage take the masked path outside the
+      // loop over the full prefix stages.  The loop then has a single code path, so its
+      // O accumulators stay in place (where two paths join inside a loop the compiler
+      // copies all of them on every iteration).
+      int st = 0;
+      if (has_tree) {
+        begin_stage(0);
+        stage_fast(0);
+        st = 1;
+      }
+      const int full_end = has_tree + n_full;
+      auto full_loop = [&](auto ntile_tag) {
+        for (; st < full_end; ++st) {
+          begin_stage(st);
+          stage_full(ntile_tag, st);
+        }
+      };
+      if (QT > 1 && live1) full_loop(ic<QT>{});
+      else full_loop(ic<1>{});
+      if (st < nst) {
         begin_stage(st);
         stage_fast(st);
       }
