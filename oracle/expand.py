@@ -164,3 +164,62 @@ def expand_rerank(logits_steps, k, m, root_token, n_max=64, budget_log=None):
         n_nodes[b] = 1 + len(kept)
         status[b] = STATUS_OK
     return ExpandResult(parent, token, score, n_nodes, status, frontier_tokens, indeterminate)
+
+
+def draft_continue(logits_steps, k, m, budget_log=None, n_max=64):
+    """The harness's per-level stop.  "Technical analysis of EAGLE-4", section "EAGLE-4
+    verification trees and the harness": at each draft level the gain in cumulative
+    probability per unit of measured marginal verification cost decides whether the
+    tree is drafted further; drafting stops once it falls below the threshold.
+
+    Reading (listed in the design doc): after level s, let c be the best child that level
+    created (its frontier node of rank 0) and p its place in the whole pool ranked
+    best first by (score descending, creation ascending).  Drafting goes on when c
+    would be kept by the final rerank if drafting stopped now: p <= m - 1 and the
+    places 1..p all pass the verify budget (budget_cut).  A deeper node scores no
+    better than its parent and is created after it, so it ranks after c; when c is
+    not kept no later level can add a kept node, and stopping leaves the final tree
+    unchanged.
+
+    Returns int32 [S][B]: more[s][b] after level s + 1 (0 for a failed sequence and
+    for every level from the failing one on).  The levels are expanded with the same
+    arithmetic as expand_rerank."""
+    S = len(logits_steps)
+    B = logits_steps[0].shape[0]
+    m_arr = np.broadcast_to(np.asarray(m, dtype=np.int64), (B,))
+    more = np.zeros((S, B), dtype=np.int32)
+    for b in range(B):
+        mb = int(m_arr[b])
+        pool = []                                  # (score, creation) of every child
+        frontier = [(np.float32(0.0),)]            # scores of the frontier, best first
+        for s in range(S):
+            rows = logits_steps[s][b]
+            children = []
+            bad = False
+            for f, (fscore,) in enumerate(frontier):
+                row = np.asarray(rows[f], dtype=np.float32)
+                if not np.all(np.isfinite(row)):
+                    bad = True
+                    break
+                lse32, _ = row_log_normaliser(row)
+                for t in row_topk(row, k):
+                    sc = np.float32(fscore + np.float32(row[t] - lse32))
+                    children.append((sc, len(pool) + len(children)))
+            if bad:
+                break
+            pool.extend(children)
+            ranked = sorted(children, key=lambda c: rank_key(c[0], c[1]))
+            frontier = [(c[0],) for c in ranked[:k]]
+            best = ranked[0]
+            order = sorted(pool, key=lambda c: rank_key(c[0], c[1]))
+            p = 1 + order.index(best)
+            run = p if budget_log is None else budget_cut([c[0] for c in order[:p]], budget_log)
+            more[s, b] = int(1 <= mb <= n_max and best_child_kept(p, mb, run))
+    return more
+
+
+def best_child_kept(place, m, run):
+    """The level's best child, at `place` (1-based) in the best-first pool, is kept by
+    the final rerank: it is among the m - 1 candidates and the budget's leading run of
+    passing places (`run` long, counted over places 1..place) reaches it."""
+    return place <= m - 1 and run == place

@@ -714,6 +714,83 @@ def pin_budget_first_failure_stops():
     return bool(np.all(cut.n_nodes == 3)) and bool(np.all(plain.n_nodes == 12))
 
 
+
+# ------------------------------------------------------------------ per-level stop
+
+def _stop_cases(seed):
+    """Small dynamic trees (quantised logits: ties common) with verify budgets from a
+    convex synthetic cost table, plus the two extreme budgets and none."""
+    rng = np.random.default_rng(seed)
+    for t in range(6):
+        B, k, S, V = 4, [2, 3, 4][t % 3], 5, [20, 40, 60][t % 3]
+        steps = _levels(rng, B, S, k, V, quant=t % 2 == 0)
+        m = rng.integers(2, 40, size=B)
+        j = np.arange(64, dtype=np.float64)
+        marginal = 0.05 + 0.02 * j                         # d/dN of a convex cost table
+        for bar in (np.log(10.0 ** rng.uniform(-4, -1) * marginal).astype(np.float32),
+                    np.full(64, -np.inf, np.float32), np.full(64, np.inf, np.float32), None):
+            if bar is not None:
+                bar[0] = -np.inf
+            yield steps, k, m, bar, rng.integers(0, V, size=B)
+
+
+def _depth(parent_row, i):
+    d = 0
+    while i > 0:
+        i = int(parent_row[i])
+        d += 1
+    return d
+
+
+def pin_stop_means_deepest_level_kept(seed=71):
+    """more[s][b] = 1 exactly when the tree reranked right after level s + 1 keeps a
+    node of that level (the deepest level drafted so far)."""
+    for steps, k, m, bar, roots in _stop_cases(seed):
+        more = oracle.expand.draft_continue(steps, k, m, bar)
+        for s in range(len(steps)):
+            res = oracle.expand_rerank(steps[:s + 1], k, m, roots, budget_log=bar)
+            for b in range(len(m)):
+                deepest = max(_depth(res.parent[b], i) for i in range(int(res.n_nodes[b])))
+                if int(more[s, b]) != int(deepest == s + 1):
+                    return False
+    return True
+
+
+def pin_stop_is_lossless(seed=72):
+    """Stopping at the first level whose flag is 0 and reranking there gives the same
+    tree as drafting every level."""
+    seen = 0
+    for steps, k, m, bar, roots in _stop_cases(seed):
+        more = oracle.expand.draft_continue(steps, k, m, bar)
+        full = oracle.expand_rerank(steps, k, m, roots, budget_log=bar)
+        for b in range(len(m)):
+            zeros = np.flatnonzero(more[:, b] == 0)
+            if len(zeros) == 0 or zeros[0] == len(steps) - 1:
+                continue
+            s0 = int(zeros[0])
+            cut = oracle.expand_rerank(steps[:s0 + 1], k, m, roots, budget_log=bar)
+            seen += 1
+            if not (cut.n_nodes[b] == full.n_nodes[b] and np.array_equal(cut.parent[b], full.parent[b])
+                    and np.array_equal(cut.token[b], full.token[b])
+                    and cut.score[b].tobytes() == full.score[b].tobytes()):
+                return False
+    return seen >= 20                          # the stop is exercised, not vacuous
+
+
+def pin_stop_limits():
+    """A budget of +inf stops at once; a failing row gives 0 from its level on; m = 1
+    never drafts."""
+    steps, k, roots = _budget_case(63)
+    hi = oracle.expand.draft_continue(steps, k, 20, np.full(64, np.inf, np.float32))
+    one = oracle.expand.draft_continue(steps, k, 1, None)
+    bad = [x.copy() for x in steps]
+    bad[2][1, 0, 3] = np.inf
+    nf = oracle.expand.draft_continue(bad, k, 63, None)
+    ok = not hi.any() and not one.any()
+    ok &= bool(np.all(nf[:2, 1] == 1)) and bool(np.all(nf[2:, 1] == 0)) and bool(np.all(nf[:, 0] == 1))
+    return bool(ok)
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -742,6 +819,9 @@ ALL_PINS = {
     "stochastic_preserves_target": pin_stochastic_preserves_target,
     "budget_limits": pin_budget_limits,
     "budget_first_failure_stops": pin_budget_first_failure_stops,
+    "stop_means_deepest_level_kept": pin_stop_means_deepest_level_kept,
+    "stop_is_lossless": pin_stop_is_lossless,
+    "stop_limits": pin_stop_limits,
 }
 
 

@@ -100,6 +100,10 @@ MUTATIONS = {
         (oracle.expand, "budget_cut", lambda sc, bl: sum(1 for j, x in enumerate(sc, 1) if np.float32(x) > bl[j]))],
     "budget: a tie passes": [
         (oracle.expand, "budget_cut", lambda sc, bl: next((j - 1 for j, x in enumerate(sc, 1) if not np.float32(x) >= bl[j]), len(sc)))],
+    "stop: the m - 1 bound taken as strict": [
+        (oracle.expand, "best_child_kept", lambda place, m, run: place < m - 1 and run == place)],
+    "stop: the verify budget ignored": [
+        (oracle.expand, "best_child_kept", lambda place, m, run: place <= m - 1)],
     "compact: one node short": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }
