@@ -213,7 +213,10 @@ def draft_continue(logits_steps, k, m, budget_log=None, n_max=64):
             best = ranked[0]
             order = sorted(pool, key=lambda c: rank_key(c[0], c[1]))
             p = 1 + order.index(best)
-            run = p if budget_log is None else budget_cut([c[0] for c in order[:p]], budget_log)
+            run = p
+            if budget_log is not None:
+                # one bar per place up to n_max - 1; a place past them is never kept (m <= n_max)
+                run = budget_cut([c[0] for c in order[:p]], budget_log) if p < len(budget_log) else 0
             more[s, b] = int(1 <= mb <= n_max and best_child_kept(p, mb, run))
     return more
 

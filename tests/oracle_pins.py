@@ -721,10 +721,10 @@ def _stop_cases(seed):
     """Small dynamic trees (quantised logits: ties common) with verify budgets from a
     convex synthetic cost table, plus the two extreme budgets and none."""
     rng = np.random.default_rng(seed)
-    for t in range(6):
-        B, k, S, V = 4, [2, 3, 4][t % 3], 5, [20, 40, 60][t % 3]
+    for t in range(8):
+        B, k, S, V = 4, [2, 3, 4, 8][t % 4], [5, 5, 5, 4][t % 4], [20, 40, 60, 100][t % 4]
         steps = _levels(rng, B, S, k, V, quant=t % 2 == 0)
-        m = rng.integers(2, 40, size=B)
+        m = rng.integers(2, 65, size=B)
         j = np.arange(64, dtype=np.float64)
         marginal = 0.05 + 0.02 * j                         # d/dN of a convex cost table
         for bar in (np.log(10.0 ** rng.uniform(-4, -1) * marginal).astype(np.float32),
