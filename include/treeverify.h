@@ -138,6 +138,31 @@ tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int max_st
                              int32_t* frontier_token, int32_t* seq_status, hipStream_t stream);
 
 /*
+ * tree_draft_continue -- the harness's per-level stop.  [EAGLE-4] "verification trees
+ * and the harness": at each draft level the gain in cumulative probability per unit
+ * of measured marginal verification cost decides whether the tree is drafted
+ * further.  Call after tree_expand_rerank of any level, on the same workspace and
+ * with the same k and max_steps.  For sequence b, let c be the best child created by
+ * the latest level (its frontier node of rank 0) and p its place in the whole pool
+ * ranked best first by (score descending, creation ascending):
+ *   more[b] = 1 when p <= m_b - 1 and every place j = 1..p passes the verify budget
+ *             (its score > budget_log[j]; no budget when budget_log is NULL), i.e. c
+ *             would be kept by the final rerank if drafting stopped now;
+ *   more[b] = 0 otherwise, and for a failed sequence or m_b < 2.
+ * A deeper node scores no better than its parent and ranks after it, so once more[b]
+ * is 0 no later level adds a node to the reranked tree: the caller may stop drafting
+ * that sequence (or keep drafting it with the batch) without changing its tree.
+ *   m_b = m_per_seq[b] (device, nullable) else m; budget_log float32 [64] device,
+ *   nullable, as for tree_expand_rerank; more int32 [B] device out.
+ * Errors: TV_ERR_NULL (more), TV_ERR_SHAPE (B, k, max_steps, m outside 0..64, or
+ * m < 1 without m_per_seq), TV_ERR_WORKSPACE (ws NULL or smaller than
+ * tree_expand_workspace_size(B, k, max_steps)).
+ */
+tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int max_steps, int m,
+                              const int32_t* m_per_seq, const float* budget_log, int32_t* more,
+                              hipStream_t stream);
+
+/*
  * tree_budget_thresholds -- the per-place bars of the verify budget (HOST pointers,
  * no device work).  [EAGLE-4] "verification trees and the harness": a calibrated cost
  * table (verification latency against batch, context length and candidate count)

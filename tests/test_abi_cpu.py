@@ -85,6 +85,21 @@ def test_expand_validation(L):
     assert _expand(L, ws_bytes=need - 1) == WS
 
 
+def test_draft_continue_validation(L):
+    need = L.tree_expand_workspace_size(2, 4, 3)
+    f = lambda ws=P, ws_bytes=need, B=2, k=4, S=3, m=8, mps=Z, more=P: L.tree_draft_continue(
+        ws, ws_bytes, B, k, S, m, mps, Z, more, Z)
+    assert f(more=Z) == NULL
+    assert f(B=0) == SHAPE
+    assert f(k=17) == SHAPE
+    assert f(S=0) == SHAPE
+    assert f(m=65) == SHAPE
+    assert f(m=0) == SHAPE                       # no m at all
+    assert f(k=16, S=20) == SHAPE                # pool beyond 4096 slots
+    assert f(ws=Z) == WS
+    assert f(ws_bytes=need - 1) == WS
+
+
 def test_expand_workspace_size(L):
     assert L.tree_expand_workspace_size(0, 4, 3) == 0
     assert L.tree_expand_workspace_size(1, 17, 3) == 0

@@ -556,3 +556,63 @@ def test_expand_budget_limits_on_device():
     for bar in (np.full(64, -np.inf, np.float32), np.full(64, np.inf, np.float32)):
         ref = _check_expand(levels, 6, 40, roots, budget_log=bar)
         assert np.all(ref.n_nodes == (40 if bar[1] < 0 else 1))
+
+
+# ----------------------------------------------------------------------------- per-level stop
+
+def _stop_on_device(levels, k, m, m_per_seq, bar):
+    """Every level of tree_expand_rerank, each followed by tree_draft_continue; returns
+    the flags [S][B]."""
+    B, S = levels[0].shape[0], len(levels)
+    ws = tv.expand_workspace(B, k, S)
+    out = tv.ExpandOutputs(B, 64, k, DEV)
+    roots = dev_i32(np.zeros(B, np.int32))
+    mps = None if m_per_seq is None else dev_i32(m_per_seq)
+    bud = None if bar is None else torch.from_numpy(np.ascontiguousarray(bar, np.float32)).to(DEV)
+    flags = []
+    for s in range(S):
+        final = (m if m_per_seq is None else 64) if s == S - 1 else 0
+        tv.tree_expand_rerank(ws, s + 1, torch.from_numpy(levels[s]).to(DEV), k, S, final_m=int(final),
+                              m_per_seq=mps, root_token=roots, out=out, budget_log=bud)
+        more = tv.tree_draft_continue(ws, B, k, S, m=0 if m_per_seq is not None else m,
+                                      m_per_seq=mps, budget_log=bud)
+        flags.append(more.cpu().numpy().copy())
+    return np.stack(flags)
+
+
+def _bars(rng):
+    cost = (20.0 + 0.05 * np.arange(1, 65) + 0.01 * np.arange(1, 65) ** 2).astype(np.float32)
+    return [tv.budget_thresholds(cost, float(10.0 ** rng.uniform(-4, -1.5))),
+            np.full(64, -np.inf, np.float32), np.full(64, np.inf, np.float32), None]
+
+
+@pytest.mark.parametrize("seed,B,k,S,V,tied", [(1, 4, 2, 6, 40, True), (2, 6, 4, 5, 300, False),
+                                              (3, 3, 8, 4, 2000, True), (4, 8, 10, 4, 32000, False)])
+def test_draft_continue_matches_oracle(seed, B, k, S, V, tied):
+    rng = np.random.default_rng(seed)
+    levels = []
+    for s in range(S):
+        shape = (B, 1 if s == 0 else k, V)
+        levels.append((rng.integers(-6, 6, size=shape) * 0.5).astype(np.float32) if tied
+                      else (rng.standard_normal(shape) * 2).astype(np.float32))
+    m_seq = rng.integers(2, 64, size=B).astype(np.int32)
+    for bar in _bars(rng):
+        for m, mps in ((int(m_seq[0]), None), (0, m_seq)):
+            ref = oracle.expand.draft_continue(levels, k, m if mps is None else mps, bar)
+            got = _stop_on_device(levels, k, m, mps, bar)
+            assert np.array_equal(got, ref), (bar is None, m, got.T, ref.T)
+
+
+@pytest.mark.parametrize("wid", [3, 5])
+def test_draft_continue_workload(wid):
+    """Workloads 3 and 5 with a verify budget from a cost table: the device's flags equal
+    the oracle's after every level, and some sequence stops before the last level."""
+    w = synth.WORKLOADS[wid]
+    cost = np.concatenate([np.full(16, 20.0), 20.0 + 0.5 * np.arange(1, 49)]).astype(np.float32)
+    bar = tv.budget_thresholds(cost, 1e-3)
+    kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+    levels = synth.draft_logits(w)
+    ref = oracle.expand.draft_continue(levels, w.k, w.m if kc is None else kc, bar)
+    got = _stop_on_device(levels, w.k, w.m if kc is None else 0, kc, bar)
+    assert np.array_equal(got, ref)
+    assert np.any(ref[:-1] == 0)

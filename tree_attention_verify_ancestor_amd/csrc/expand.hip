@@ -8,7 +8,7 @@
 // float32, then fl32(parent + fl32(logit - lse)).  Every score bit is thereby fixed,
 // so the kept set is exactly reproducible.
 //
-// Two kernels per call:
+// Two kernels per call (and a third, draft_continue_kernel, for the per-level stop):
 //   expand_rows_kernel   grid (chunk, frontier row, sequence).  Each workgroup reads
 //                        one chunk of one logit row once (coalesced loads held in
 //                        registers) and records the chunk's maximum, its float64 sum of
@@ -612,6 +612,62 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   }
 }
 
+// The harness's per-level stop, one workgroup per sequence, after a level's select
+// kernel: the latest level's best child (the frontier's rank 0) is at place p of the
+// pool ranked best first; drafting goes on when p <= m - 1 and every place 1..p
+// passes the verify budget, i.e. when that child would be kept if drafting stopped
+// now.  Deeper nodes rank after their parents, so a 0 here never changes the tree.
+__global__ __launch_bounds__(kSelThreads) void draft_continue_kernel(
+    const char* __restrict__ ws, size_t stride, int m, const int32_t* __restrict__ m_per_seq,
+    const float* __restrict__ budget_log, int32_t* __restrict__ more) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const char* seq = ws + (size_t)b * stride;
+  const SeqHeader* hdr = (const SeqHeader*)seq;
+  const PoolEntry* pool = (const PoolEntry*)(seq + sizeof(SeqHeader));
+  __shared__ float s_sc[kPoolMax];
+  __shared__ int s_place, s_fail;
+
+  const int st = hdr->status;
+  const int count = hdr->count;
+  const int cs = hdr->frontier[0];
+  const int mb = m_per_seq ? m_per_seq[b] : m;
+  if (st != TV_SEQ_OK || count < 1 || count > kPoolMax || cs < 0 || cs >= count || mb < 2 ||
+      mb > TV_MAX_NODES) {
+    if (tid == 0) more[b] = 0;
+    return;
+  }
+  if (tid == 0) {
+    s_place = 1;
+    s_fail = 0;
+  }
+  for (int c = tid; c < count; c += kSelThreads) s_sc[c] = pool[c].score;
+  __syncthreads();
+  const float ss = s_sc[cs];
+  int ahead = 0;
+  for (int c = tid; c < count; c += kSelThreads) ahead += better(s_sc[c], c, ss, cs);
+  if (ahead) atomicAdd(&s_place, ahead);
+  __syncthreads();
+  const int place = s_place;
+  if (place > mb - 1) {                                   // beyond the kept count
+    if (tid == 0) more[b] = 0;
+    return;
+  }
+  if (budget_log) {
+    // places 1..place hold the child itself and the entries ranked before it; each
+    // must pass the bar of its own place
+    for (int c = tid; c < count; c += kSelThreads) {
+      const float sc = s_sc[c];
+      if (c != cs && !better(sc, c, ss, cs)) continue;
+      int r = 0;
+      for (int o = 0; o < count; ++o) r += better(s_sc[o], o, sc, c);
+      if (!(sc > budget_log[r + 1])) s_fail = 1;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) more[b] = s_fail ? 0 : 1;
+}
+
 // Chunking of a logit row: about 1024 workgroups in all, each chunk between 1024 and
 // 8192 logits where the vocabulary allows, at most kMaxRowChunks chunks per row.
 struct RowPlan {
@@ -690,6 +746,22 @@ TV_API tv_status tree_expand_rerank(void* ws, size_t ws_bytes, int B, int k, int
                      (char*)ws, stride, rec_off, k, step, rows, rp.nch, final_m, m_per_seq,
                      budget_log, root_token, n_max, parent, token, score, n_nodes, frontier_token,
                      seq_status);
+  return tv::launch_status();
+}
+
+TV_API tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int max_steps,
+                                     int m, const int32_t* m_per_seq, const float* budget_log,
+                                     int32_t* more, hipStream_t stream) {
+  if (!more) return TV_ERR_NULL;
+  if (B < 1 || k < 1 || k > tv::kTopKMax || max_steps < 1 || m < 0 || m > TV_MAX_NODES ||
+      (!m_per_seq && m < 1))
+    return TV_ERR_SHAPE;
+  if (tv::pool_capacity(k, max_steps) > tv::kPoolMax) return TV_ERR_SHAPE;
+  const size_t need = tree_expand_workspace_size(B, k, max_steps);
+  if (!ws || ws_bytes < need) return TV_ERR_WORKSPACE;
+  hipLaunchKernelGGL(tv::draft_continue_kernel, dim3(B), dim3(tv::kSelThreads), 0, stream,
+                     (const char*)ws, tv::seq_stride_bytes(k, max_steps), m, m_per_seq, budget_log,
+                     more);
   return tv::launch_status();
 }
 

@@ -106,6 +106,22 @@ def tree_expand_rerank(ws, step, logits, k, max_steps, final_m=0, m_per_seq=None
     return out
 
 
+def tree_draft_continue(ws, B, k, max_steps, m=0, m_per_seq=None, budget_log=None, more=None):
+    """The per-level stop after a tree_expand_rerank level on workspace `ws`: int32 [B],
+    1 where drafting that sequence further may still change its reranked tree."""
+    _need(ws, "ws", torch.uint8, 1)
+    if m_per_seq is not None:
+        _need(m_per_seq, "m_per_seq", torch.int32, shape=(B,))
+    if budget_log is not None:
+        _need(budget_log, "budget_log", torch.float32, shape=(64,))
+    if more is None:
+        more = torch.empty((B,), dtype=torch.int32, device=ws.device)
+    check("tree_draft_continue", lib().tree_draft_continue(
+        _ptr(ws), ws.numel(), B, k, max_steps, m, _ptr(m_per_seq), _ptr(budget_log), _ptr(more),
+        _stream()))
+    return more
+
+
 def budget_thresholds(cost_us, threshold):
     """Per-place bars of the verify budget from a cost table: cost_us[N-1] = latency of
     one tree_verify_attn call with N nodes per tree (N = 1..n_max).  Returns a host
