@@ -110,10 +110,12 @@ tv_status tree_build(int B, int n_max, const int32_t* parent, const int32_t* n_n
  * log-confidence (log of the value).  Children are numbered in creation order
  * (row, then top-k rank).  The next frontier is the k best children of this level
  * by (score descending, creation ascending).
- * When final_m > 0 (the last level), the whole pool of children is reranked: the
- * m - 1 best by the same order are kept with the root (m = m_per_seq[b] if that
- * pointer is given, else final_m), and written root first, then by (depth,
- * creation), with parents remapped to output indices:
+ * When final_m > 0 (the last level, or any level whose tree the caller may keep, as
+ * with the per-level stop of tree_draft_continue), the whole pool of children so far
+ * is reranked: the m - 1 best by the same order are kept with the root (m =
+ * m_per_seq[b] if that pointer is given, else final_m), and written root first, then
+ * by (depth, creation), with parents remapped to output indices (a later level may
+ * still follow on the same workspace):
  *   parent int32 [B][n_max], token int32 [B][n_max] (token[b][0] = root_token[b]),
  *   score fp32 [B][n_max] (root 0), n_nodes int32 [B]; padding -1 / -1 / 0.
  * budget_log float32 [64] (device, nullable; last level only) is a verify budget

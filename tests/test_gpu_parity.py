@@ -616,3 +616,47 @@ def test_draft_continue_workload(wid):
     got = _stop_on_device(levels, w.k, w.m if kc is None else 0, kc, bar)
     assert np.array_equal(got, ref)
     assert np.any(ref[:-1] == 0)
+
+
+def test_expand_rerank_at_every_level():
+    """final_m at every level: after each level the outputs hold the oracle's tree of
+    the levels done so far, and the next level continues on the same workspace."""
+    rng = np.random.default_rng(81)
+    B, k, S, V = 5, 4, 5, 700
+    levels = [(rng.standard_normal((B, 1 if s == 0 else k, V)) * 2).astype(np.float32) for s in range(S)]
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    m_seq = np.array([2, 9, 30, 64, 17], np.int32)
+    ws = tv.expand_workspace(B, k, S)
+    out = tv.ExpandOutputs(B, 64, k, DEV)
+    for s in range(S):
+        tv.tree_expand_rerank(ws, s + 1, torch.from_numpy(levels[s]).to(DEV), k, S, final_m=64,
+                              m_per_seq=dev_i32(m_seq), root_token=dev_i32(roots), out=out)
+        ref = oracle.expand_rerank(levels[:s + 1], k, m_seq, roots)
+        assert np.array_equal(out.n_nodes.cpu().numpy(), ref.n_nodes)
+        assert np.array_equal(out.parent.cpu().numpy(), ref.parent)
+        assert np.array_equal(out.token.cpu().numpy(), ref.token)
+        assert out.score.cpu().numpy().tobytes() == ref.score.tobytes()
+
+
+@pytest.mark.parametrize("wid", [3, 5])
+def test_draft_tree_stops_without_changing_the_tree(wid):
+    """The harness's drafting loop stops before the last level on the EAGLE-2 and
+    serving workloads under a cost-table budget, and its tree equals the oracle's tree
+    over every level."""
+    from tree_attention_verify_ancestor_amd import harness
+    w = synth.WORKLOADS[wid]
+    cost = np.concatenate([np.full(16, 20.0), 20.0 + 0.5 * np.arange(1, 49)]).astype(np.float32)
+    bar = tv.budget_thresholds(cost, 1e-3)
+    kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
+    levels = synth.draft_logits(w)
+    roots = synth.root_tokens(w)
+    out, drafted = harness.draft_tree(
+        lambda step, front: torch.from_numpy(levels[step - 1]).to(DEV), w.B, w.k, w.S,
+        m=w.m if kc is None else 0, m_per_seq=None if kc is None else dev_i32(kc),
+        budget_log=torch.from_numpy(bar).to(DEV), root_token=dev_i32(roots))
+    ref = oracle.expand_rerank(levels, w.k, w.m if kc is None else kc, roots, budget_log=bar)
+    assert drafted < w.S
+    assert np.array_equal(out.n_nodes.cpu().numpy(), ref.n_nodes)
+    assert np.array_equal(out.parent.cpu().numpy(), ref.parent)
+    assert np.array_equal(out.token.cpu().numpy(), ref.token)
+    assert out.score.cpu().numpy().tobytes() == ref.score.tobytes()

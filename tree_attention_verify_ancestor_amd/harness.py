@@ -4,10 +4,11 @@
 harness": before serving, a one-time calibration on the target GPU builds a table of
 verification latency against batch size, context length and candidate count; the
 harness then adds candidates while the gain in cumulative probability per unit of
-marginal cost stays above a threshold.  calibrate() measures this library's own
-tree_verify_attn (HIP events around graph replays) at one (batch, context) for a few
-node counts and interpolates the rest; budget_thresholds() (the library's host
-helper) turns the table into the per-place bars tree_expand_rerank takes.
+marginal cost stays above a threshold, and stops drafting once it falls below.
+calibrate() measures this library's own tree_verify_attn (HIP events around graph
+replays) at one (batch, context) for a few node counts and interpolates the rest; budget_thresholds() (the library's host
+helper) turns the table into the per-place bars tree_expand_rerank takes;
+draft_tree() drafts level by level and stops with tree_draft_continue.
 
 Usage: python -m tree_attention_verify_ancestor_amd.harness   (prints JSON tables)
 """
@@ -65,6 +66,36 @@ def calibrate(B, L, Hq, Hkv, D=128, n_points=DEFAULT_N, reps=20, device="cuda", 
 
 def budget_thresholds(cost_us, threshold):
     return ops.budget_thresholds(cost_us, threshold)
+
+
+def draft_tree(level_logits, B, k, max_steps, m=0, m_per_seq=None, budget_log=None,
+               root_token=None, n_max=64, ws=None, out=None):
+    """The harness's drafting loop: expand level by level, rerank after every level
+    (final_m at each call, so `out` always holds the tree of the levels done), and stop
+    once tree_draft_continue reports for every sequence that another level cannot change
+    its tree -- the harness's "decide when to stop drafting".
+
+    level_logits(step, frontier_token) -> fp32 [B][1 if step == 1 else k][vocab]: the
+    drafter's logits for the frontier of the previous level (frontier_token [B][k], the
+    tokens by rank).  Reading the flags costs one host synchronisation per level.
+    Returns (out, levels drafted)."""
+    dev = root_token.device if root_token is not None else "cuda"
+    if ws is None:
+        ws = ops.expand_workspace(B, k, max_steps, dev)
+    if out is None:
+        out = ops.ExpandOutputs(B, n_max, k, dev)
+    final = m if m_per_seq is None else n_max
+    for step in range(1, max_steps + 1):
+        ops.tree_expand_rerank(ws, step, level_logits(step, out.frontier_token), k, max_steps,
+                               final_m=final, m_per_seq=m_per_seq, root_token=root_token,
+                               n_max=n_max, out=out, budget_log=budget_log)
+        if step == max_steps:
+            break
+        more = ops.tree_draft_continue(ws, B, k, max_steps, m=0 if m_per_seq is not None else m,
+                                       m_per_seq=m_per_seq, budget_log=budget_log)
+        if not bool(more.any()):
+            break
+    return out, step
 
 
 def _main():
