@@ -28,8 +28,8 @@
 //     Key-split waves merge their (m, l, O) through LDS.  The output per row and chunk
 //     is the final bf16 row when one chunk covers the prefix, else an unnormalised
 //     fp32 partial plus (m, l).
-//   attn_combine   one wave per output row merges the chunk partials, writes bf16 out
-//     and the natural-log lse.
+//   attn_combine   sixteen lanes per output row merge the chunk partials (eight chunks
+//     in flight at a time), write bf16 out and the natural-log lse.
 // fp32 path: attn_f32, one workgroup per output row on the vector ALUs (the
 // fp32 workloads are small correctness cases).
 #include <math.h>
@@ -771,14 +771,22 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   }
 }
 
-// Merge of the key-chunk partials: one wave per output row whose sequence spans more
-// than one chunk (the others were written by attn_bf16).  All partials of the row are
-// loaded first, then combined online.
+// Merge of the key-chunk partials for the rows whose sequence spans more than one
+// chunk (the others were written by attn_bf16).  Sixteen lanes per output row, four
+// rows per wave, sixteen per workgroup: a lane owns D/16 consecutive dims (16-byte
+// loads and one 8- or 16-byte store).  The partials are loaded eight chunks at a time
+// before any is used and merged online against a running maximum.
+constexpr int kCombineLanes = 16;                    // lanes per output row
+constexpr int kCombineRows = 256 / kCombineLanes;    // output rows per workgroup
+constexpr int kCombineBatch = 8;                     // chunk partials in flight per lane
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int DPL = D / kCombineLanes;             // dims per lane: 8 or 4
+  constexpr int V4 = DPL / 4;                        // f32x4 loads per lane and chunk
+  const int row = blockIdx.x * kCombineRows + threadIdx.x / kCombineLanes;
   if (row >= a.B * a.n_max * a.Hq) return;
-  const int lane = threadIdx.x & 63;
+  const int d0 = (threadIdx.x % kCombineLanes) * DPL;
   const int h = row % a.Hq;
   const int i = (row / a.Hq) % a.n_max;
   const int b = row / (a.Hq * a.n_max);
@@ -794,39 +802,52 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int rb = rho / a.rows_per_wg;
   const int unit = (b * a.Hkv + kvh) * a.n_rb + rb;
   const size_t slot0 = (size_t)unit * a.n_chunks * a.rows_per_wg + rho % a.rows_per_wg;
-  constexpr int PL = D / 64;                            // dims per lane
-  float2 ml[kMaxChunks];
-  float pv[kMaxChunks][PL];
+  float M = -INFINITY, wsum = 0.f;
+  f32x4 acc[V4];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < nc) {
-      const size_t slot = slot0 + (size_t)c * a.rows_per_wg;
-      ml[c] = a.part_ml[slot];
+  for (int v = 0; v < V4; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nc; c0 += kCombineBatch) {
+    float2 ml[kCombineBatch];
+    f32x4 po[kCombineBatch][V4];
 #pragma unroll
-      for (int e = 0; e < PL; ++e) pv[c][e] = a.part_o[slot * D + lane * PL + e];
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (c0 + j < nc) {
+        const size_t slot = slot0 + (size_t)(c0 + j) * a.rows_per_wg;
+        ml[j] = a.part_ml[slot];
+#pragma unroll
+        for (int v = 0; v < V4; ++v) po[j][v] = *(const f32x4*)(a.part_o + slot * D + d0 + 4 * v);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.f);
+      }
     }
-  }
-  float M = -INFINITY, wsum = 0.f, acc[PL];
+    float mn = M;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
+    for (int j = 0; j < kCombineBatch; ++j) mn = fmaxf(mn, ml[j].x);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float sa = __builtin_amdgcn_exp2f(M - ms);          // 0 while nothing was merged
+    wsum *= sa;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < nc) {
-      const float mn = fmaxf(M, ml[c].x);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      const float sa = __builtin_amdgcn_exp2f(M - ms);
-      const float sb = __builtin_amdgcn_exp2f(ml[c].x - ms);
+    for (int v = 0; v < V4; ++v) acc[v] *= sa;
 #pragma unroll
-      for (int e = 0; e < PL; ++e) acc[e] = acc[e] * sa + pv[c][e] * sb;
-      wsum = wsum * sa + ml[c].y * sb;
-      M = mn;
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (c0 + j < nc) {
+        const float sb = __builtin_amdgcn_exp2f(ml[j].x - ms);  // 0 for a chunk without keys
+        wsum += ml[j].y * sb;
+#pragma unroll
+        for (int v = 0; v < V4; ++v) acc[v] += po[j][v] * sb;
+      }
     }
+    M = mn;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  __bf16* op = a.out + (size_t)row * D + lane * PL;
+  __bf16 ob[DPL];
 #pragma unroll
-  for (int e = 0; e < PL; ++e) op[e] = (__bf16)(acc[e] * inv);
-  if (a.lse && lane == 0) a.lse[row] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : 0.f;
+  for (int v = 0; v < V4; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ob[4 * v + e] = (__bf16)(acc[v][e] * inv);
+  if constexpr (DPL == 8) *(bf16x8*)(a.out + (size_t)row * D + d0) = *(const bf16x8*)ob;
+  else *(s16x4*)(a.out + (size_t)row * D + d0) = *(const s16x4*)ob;
+  if (a.lse && d0 == 0) a.lse[row] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : 0.f;
 }
 
 // fp32 inputs: one workgroup of 128 threads per output row, vector ALUs only.
@@ -929,7 +950,8 @@ static void launch_bf16(const AttnPlan& p, const AttnArgs& a, hipStream_t stream
   else hipLaunchKernelGGL((attn_bf16<D, 8, 1, 1>), grid, block, 0, stream, a);
   if (p.n_chunks > 1) {
     const int rows = a.B * a.n_max * a.Hq;
-    hipLaunchKernelGGL(attn_combine<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_combine<D>, dim3((rows + kCombineRows - 1) / kCombineRows), dim3(256), 0,
+                       stream, a);
   }
 }
 
