@@ -200,6 +200,11 @@ SMALL_ATTN = [  # (B, Hq, Hkv, D, prefix lengths, node counts)
     # 65..128 rows per KV head (eight waves as four row groups x two key halves)
     (2, 4, 2, 64, (300, 1000), (64, 40)),
     (1, 6, 3, 128, (777,), (50,)),
+    # eight or more sequences: ragged ones take their (sequence, chunk) pairs by work
+    (9, 8, 2, 128, (3000, 17, 0, 900, 2500, 64, 1200, 5, 640), (64, 3, 20, 64, 1, 33, 50, 64, 10)),
+    (12, 16, 4, 64, (100, 2000, 50, 700, 1, 0, 3000, 256, 128, 900, 1500, 30),
+     (5, 64, 30, 12, 64, 2, 40, 64, 7, 19, 64, 26)),
+    (8, 4, 4, 64, (500,) * 8, (20,) * 8),
 ]
 
 

@@ -61,6 +61,7 @@ struct AttnArgs {
   float2* part_ml;    // [unit][chunk][row in unit]      (reference max in log2 units, sum)
   int B, Hq, Hkv, G, n_max, max_prefix;
   int rows_per_wg, chunk_keys, n_chunks, n_rb, total_wgs;
+  int rank_pairs;     // ragged batches: (sequence, chunk) pairs ranked by work in-kernel
   float sl2;          // scale * log2(e)
 };
 
@@ -70,6 +71,8 @@ struct AttnPlan {
 };
 
 constexpr int kMaxChunks = 32;                       // key chunks per work unit (merge width)
+constexpr int kMaxRankPairs = 256;                   // (sequence, chunk) pairs ranked in-kernel
+constexpr int kRankMinBatch = 8;                     // sequences from which they are ranked
 constexpr int kLdsBudget = 128 * 1024;               // the ring of prefix stages
 constexpr int kLdsMax = 160 * 1024;                  // LDS of one CU
 
@@ -209,14 +212,67 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   // workgroups running together read the same token range of every head, i.e. whole
   // contiguous prefix rows, and the row blocks of one (head, chunk) stay close in time.
   // The blockIdx -> item map is XCD-aware: consecutive items land on one XCD (and L2).
+  // A ragged batch (prefix lengths or node counts that differ) instead takes its
+  // (sequence, chunk) pairs in order of their work, keys times row tiles, largest
+  // first: the longest items are dispatched first and the short ones fill in at the
+  // end.  Every workgroup ranks the pairs itself (the stage ring is not in use yet and
+  // holds the ranking) and takes the pair at its place; consecutive workgroups take
+  // the KV heads and row blocks of one pair.
   const int x = blockIdx.x;
-  const int logical = (x % 8) * (gridDim.x / 8) + x / 8;
-  if (logical >= a.total_wgs) return;                // padding of the grid: no item
-  int t = logical;
-  const int kvh = t % a.Hkv; t /= a.Hkv;
-  const int rb = t % a.n_rb; t /= a.n_rb;
-  const int chunk = t % a.n_chunks;
-  const int b = t / a.n_chunks;
+  int kvh, rb, chunk, b;
+  bool by_work = false;
+  if (a.rank_pairs) {
+    int* s_work = (int*)smem;
+    volatile int* s_pick = s_work + kMaxRankPairs;
+    volatile int* s_ragged = s_pick + 1;
+    const int per = a.Hkv * a.n_rb;
+    const int P = a.B * a.n_chunks;
+    if (threadIdx.x == 0) *s_ragged = 0;
+    __syncthreads();
+    const int n0 = a.n_nodes[0];
+    const int64_t L0 = a.offsets[1] - a.offsets[0];
+    for (int j = threadIdx.x; j < P; j += blockDim.x) {
+      const int bj = j / a.n_chunks, cj = j % a.n_chunks;
+      const int nj = a.n_nodes[bj];
+      const int64_t Lj = a.offsets[bj + 1] - a.offsets[bj];
+      if (nj != n0 || Lj != L0) *s_ragged = 1;
+      int w = 0;
+      if (nj >= 1 && nj <= a.n_max && Lj >= 0 && Lj <= a.max_prefix) {
+        const int64_t lo = (int64_t)cj * a.chunk_keys;
+        const int keys = (int)max((int64_t)0, min((int64_t)a.chunk_keys, Lj - lo)) + (cj == 0 ? nj : 0);
+        w = (cj == 0 || lo < Lj) ? keys * ((nj * a.G + 31) / 32) : 0;
+      }
+      s_work[j] = w;
+    }
+    __syncthreads();
+    by_work = *s_ragged != 0;
+    if (by_work) {
+      const int place = x / per;
+      for (int j = threadIdx.x; j < P; j += blockDim.x) {
+        const int wj = s_work[j];
+        int r = 0;
+        for (int i = 0; i < P; ++i) r += s_work[i] > wj || (s_work[i] == wj && i < j);
+        if (r == place) *s_pick = j;
+      }
+      __syncthreads();
+      if (place >= P) return;                        // padding of the grid: no item
+      const int pick = *s_pick;
+      b = pick / a.n_chunks;
+      chunk = pick % a.n_chunks;
+      kvh = (x % per) % a.Hkv;
+      rb = (x % per) / a.Hkv;
+    }
+    __syncthreads();                                 // every wave has read the ranking
+  }
+  if (!by_work) {
+    const int logical = (x % 8) * (gridDim.x / 8) + x / 8;
+    if (logical >= a.total_wgs) return;              // padding of the grid: no item
+    int t = logical;
+    kvh = t % a.Hkv; t /= a.Hkv;
+    rb = t % a.n_rb; t /= a.n_rb;
+    chunk = t % a.n_chunks;
+    b = t / a.n_chunks;
+  }
   const int unit = (b * a.Hkv + kvh) * a.n_rb + rb;
 
   const int tid = threadIdx.x;
@@ -1023,6 +1079,8 @@ TV_API tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, in
   a.n_chunks = p.n_chunks;
   a.n_rb = p.n_rb;
   a.total_wgs = p.total_wgs;
+  // ranking pays where many sequences of different lengths share the GPU
+  a.rank_pairs = B >= tv::kRankMinBatch && (long)B * p.n_chunks <= tv::kMaxRankPairs;
   a.sl2 = scale * tv::kLog2e;
   if (D == 128) tv::launch_bf16<128>(p, a, stream);
   else tv::launch_bf16<64>(p, a, stream);
