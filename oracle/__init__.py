@@ -45,10 +45,11 @@ from .expand import expand_rerank, ExpandResult
 from .accept import tree_accept
 from .compact import kv_compact, kept_nodes
 from .stochastic import tree_accept_stochastic
+from .candidates import candidate_logits
 
 __all__ = [
     "tree_build", "validate_parents", "path_to_root", "tree_verify_attn", "tree_mask",
     "expand_rerank", "ExpandResult", "tree_accept", "kv_compact", "kept_nodes",
-    "tree_accept_stochastic",
+    "tree_accept_stochastic", "candidate_logits",
     "STATUS_OK", "STATUS_BAD_PARENT", "STATUS_SECOND_ROOT", "STATUS_BAD_N", "STATUS_NONFINITE",
 ]

@@ -791,6 +791,84 @@ def pin_stop_limits():
     return bool(ok)
 
 
+
+# ------------------------------------------------------------------ low-rank candidate head
+
+def _f32_of_fraction(q):
+    """The float32 nearest to the rational q (ties to even), found without double rounding."""
+    from fractions import Fraction
+    f = np.float32(float(q))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - q)
+        key = (d, int(np.float32(c).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
+def _exact_dot_f32(u, v):
+    from fractions import Fraction
+    return _f32_of_fraction(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(u, v)))
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    return synth.bf16_to_f32(synth.bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32)))
+
+
+def pin_candidates_exact_dots(seed=91):
+    """Every logit is the exactly rounded dot product: candidates W[v].h, the others
+    Bm[v].z with z the exactly rounded A h (rational arithmetic on the bf16 values)."""
+    rng = np.random.default_rng(seed)
+    d, r, V, C = 24, 6, 40, 7
+    h = _bf16_values(rng, (2, d))
+    A, Bm, W = _bf16_values(rng, (r, d), 0.3), _bf16_values(rng, (V, r)), _bf16_values(rng, (V, d), 0.3)
+    logits, cand, _, _ = oracle.candidate_logits(h, A, Bm, W, C)
+    for i in range(2):
+        z = np.array([_exact_dot_f32(A[j], h[i]) for j in range(r)], dtype=np.float32)
+        s = np.array([_exact_dot_f32(Bm[v], z) for v in range(V)], dtype=np.float32)
+        best = sorted(range(V), key=lambda v: (-float(s[v]), v))[:C]
+        if list(cand[i]) != best:
+            return False
+        for v in range(V):
+            want = _exact_dot_f32(W[v], h[i]) if v in best else s[v]
+            if logits[i, v].tobytes() != np.float32(want).tobytes():
+                return False
+    return True
+
+
+def pin_candidates_low_rank_exact():
+    """When the LM head is exactly Bm A (small integers), the low-rank score equals the
+    full logit, so the row is the full logits row whatever C is, and the candidates
+    are its C largest (ties to the lower id)."""
+    rng = np.random.default_rng(92)
+    d, r, V = 16, 4, 30
+    A = rng.integers(-3, 4, size=(r, d)).astype(np.float32)
+    Bm = rng.integers(-3, 4, size=(V, r)).astype(np.float32)
+    W = (Bm @ A).astype(np.float32)
+    h = rng.integers(-2, 3, size=(3, d)).astype(np.float32)
+    full = (h.astype(np.float64) @ W.T.astype(np.float64)).astype(np.float32)
+    for C in (1, 5, 30):
+        logits, cand, _, _ = oracle.candidate_logits(h, A, Bm, W, C)
+        if not np.array_equal(logits, full):
+            return False
+        for i in range(3):
+            if list(cand[i]) != sorted(range(V), key=lambda v: (-float(full[i, v]), v))[:C]:
+                return False
+    return True
+
+
+def pin_candidates_all_exact():
+    """C = V: every entry is the full logit W h."""
+    rng = np.random.default_rng(93)
+    d, r, V = 32, 8, 50
+    h = _bf16_values(rng, (2, d))
+    A, Bm, W = _bf16_values(rng, (r, d)), _bf16_values(rng, (V, r)), _bf16_values(rng, (V, d))
+    logits, _, _, _ = oracle.candidate_logits(h, A, Bm, W, V)
+    return all(logits[i, v].tobytes() == _exact_dot_f32(W[v], h[i]).tobytes()
+               for i in range(2) for v in range(V))
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -822,6 +900,9 @@ ALL_PINS = {
     "stop_means_deepest_level_kept": pin_stop_means_deepest_level_kept,
     "stop_is_lossless": pin_stop_is_lossless,
     "stop_limits": pin_stop_limits,
+    "candidates_exact_dots": pin_candidates_exact_dots,
+    "candidates_low_rank_exact": pin_candidates_low_rank_exact,
+    "candidates_all_exact": pin_candidates_all_exact,
 }
 
 
