@@ -165,6 +165,28 @@ tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int
                               hipStream_t stream);
 
 /*
+ * tree_candidate_logits -- the draft model's low-rank candidate head.  [EAGLE-4]
+ * "EAGLE-4 architecture": a low-rank candidate head first scores the vocabulary in a
+ * smaller representation, then computes full logits only for the selected candidates.
+ * For every draft row i (h bf16 [rows][d], e.g. one row per frontier node):
+ *   z      = A h_i                          A  bf16 [r][d]    (float32 result)
+ *   s_v    = Bm[v] . z      for every v     Bm bf16 [vocab][r]
+ *   cand_i = the C tokens of largest s (ties to the lower id), best first
+ *   logits[i][v] = W[v] . h_i for v in cand_i, s_v elsewhere    W bf16 [vocab][d]
+ * Each dot product is a float64 sum of the exact products, rounded once to float32.
+ * The rows feed tree_expand_rerank unchanged (their log-sum-exp, top-k and scores).
+ * Outputs: logits fp32 [rows][vocab], cand int32 [rows][C].  All device pointers,
+ * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r) bytes (z), no
+ * initialisation needed.
+ * Limits: d % 8 == 0, r % 8 == 0, 8 <= r <= 512, 1 <= C <= 256, C <= vocab.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED (alignment), TV_ERR_WORKSPACE.
+ */
+size_t tree_candidate_workspace_size(int rows, int r);
+tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C, const void* h,
+                                const void* A, const void* Bm, const void* W, float* logits,
+                                int32_t* cand, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * tree_budget_thresholds -- the per-place bars of the verify budget (HOST pointers,
  * no device work).  [EAGLE-4] "verification trees and the harness": a calibrated cost
  * table (verification latency against batch, context length and candidate count)

@@ -100,6 +100,25 @@ def test_draft_continue_validation(L):
     assert f(ws_bytes=need - 1) == WS
 
 
+def test_candidate_logits_validation(L):
+    need = L.tree_candidate_workspace_size(4, 64)
+    assert need >= 4 * 64 * 4 and need % 256 == 0
+    assert L.tree_candidate_workspace_size(4, 513) == 0
+    f = lambda rows=4, d=128, r=64, V=1000, C=8, h=P, ws=P, ws_bytes=need: L.tree_candidate_logits(
+        rows, d, r, V, C, h, P, P, P, P, P, ws, ws_bytes, Z)
+    assert f(h=Z) == NULL
+    assert f(rows=0) == SHAPE
+    assert f(d=12) == SHAPE
+    assert f(r=12) == SHAPE
+    assert f(r=520) == SHAPE
+    assert f(C=0) == SHAPE
+    assert f(C=257) == SHAPE
+    assert f(V=7) == SHAPE
+    assert f(h=ctypes.c_void_p(4096 + 8)) == UNSUP
+    assert f(ws=Z) == WS
+    assert f(ws_bytes=need - 1) == WS
+
+
 def test_expand_workspace_size(L):
     assert L.tree_expand_workspace_size(0, 4, 3) == 0
     assert L.tree_expand_workspace_size(1, 17, 3) == 0

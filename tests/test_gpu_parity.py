@@ -665,3 +665,65 @@ def test_draft_tree_stops_without_changing_the_tree(wid):
     assert np.array_equal(out.parent.cpu().numpy(), ref.parent)
     assert np.array_equal(out.token.cpu().numpy(), ref.token)
     assert out.score.cpu().numpy().tobytes() == ref.score.tobytes()
+
+
+# ----------------------------------------------------------------------------- low-rank candidate head
+
+def _cand_inputs(seed, rows, d, r, V):
+    """bf16 bits of h ~ N(0,1), A ~ N(0,1/d) (z ~ N(0,1)), Bm and W scaled for logits
+    of standard deviation about 2, as the dynamic-tree workloads' draft logits."""
+    rng = np.random.default_rng(seed)
+    bits = lambda sh, sc: synth.bf16_bits((rng.standard_normal(sh) * sc).astype(np.float32))
+    return (bits((rows, d), 1.0), bits((r, d), d ** -0.5), bits((V, r), 2 * r ** -0.5),
+            bits((V, d), 2 * d ** -0.5))
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("seed,rows,d,r,V,C", [(1, 3, 72, 24, 1000, 13), (2, 10, 4096, 256, 32000, 64),
+                                              (3, 40, 512, 128, 5000, 256), (4, 2, 64, 8, 37, 37)])
+def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
+    """Bit-exact logits and candidate lists against the oracle, except entries (and
+    lists) the oracle flags as depending on the order of a float64 sum."""
+    hb, Ab, Bb, Wb = _cand_inputs(seed, rows, d, r, V)
+    f = synth.bf16_to_f32
+    ref, rc, rind, rcind = oracle.candidate_logits(f(hb), f(Ab), f(Bb), f(Wb), C)
+    lg, cd = tv.tree_candidate_logits(_bf16_dev(hb), _bf16_dev(Ab), _bf16_dev(Bb), _bf16_dev(Wb), C)
+    torch.cuda.synchronize()
+    lg, cd = lg.cpu().numpy(), cd.cpu().numpy()
+    ok = ~rind
+    assert ok.mean() > 0.99
+    assert np.array_equal(lg.view(np.uint32)[ok], ref.view(np.uint32)[ok])
+    for i in range(rows):
+        if not rcind[i]:
+            assert np.array_equal(cd[i], rc[i]), i
+    assert not rcind.all()
+
+
+def test_candidate_head_feeds_expansion():
+    """Two draft levels whose logits come from the candidate head: the device tree equals
+    the oracle's expansion of the oracle's candidate logits."""
+    k, V, d, r, C = 6, 3000, 256, 64, 32
+    hb1, Ab, Bb, Wb = _cand_inputs(8, 1, d, r, V)      # seeds whose entries are all determinate
+    hb2 = _cand_inputs(8, k, d, r, V)[0]
+    f = synth.bf16_to_f32
+    levels_ref, levels_dev = [], []
+    for hb in (hb1, hb2):
+        ref, _, rind, _ = oracle.candidate_logits(f(hb), f(Ab), f(Bb), f(Wb), C)
+        assert not rind.any()
+        levels_ref.append(ref[None])
+        lg, _ = tv.tree_candidate_logits(_bf16_dev(hb), _bf16_dev(Ab), _bf16_dev(Bb), _bf16_dev(Wb), C)
+        levels_dev.append(lg[None])
+    roots = np.array([5], np.int32)
+    ref = oracle.expand_rerank(levels_ref, k, 20, roots)
+    ws = tv.expand_workspace(1, k, 2)
+    out = tv.ExpandOutputs(1, 64, k, DEV)
+    for s in range(2):
+        tv.tree_expand_rerank(ws, s + 1, levels_dev[s], k, 2, final_m=20 if s == 1 else 0,
+                              root_token=dev_i32(roots), out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.parent.cpu().numpy(), ref.parent)
+    assert np.array_equal(out.token.cpu().numpy(), ref.token)
+    assert out.score.cpu().numpy().tobytes() == ref.score.tobytes()

@@ -3,8 +3,9 @@
 The product is libtreeverify.so (C ABI in include/treeverify.h) with the calls of
 the verification pass -- tree_build, tree_expand_rerank, tree_verify_attn,
 tree_accept -- plus tree_accept_stochastic (rejection-sampling acceptance),
-tree_kv_compact (the accepted continuation into the KV cache) and tree_draft_continue
-(the per-level stop of drafting),
+tree_kv_compact (the accepted continuation into the KV cache), tree_draft_continue
+(the per-level stop of drafting) and tree_candidate_logits (the draft model's
+low-rank candidate head),
 and this thin binding that passes torch tensors' device pointers and torch's current
 stream to it.
 """
@@ -12,9 +13,10 @@ stream to it.
 from ._lib import TreeVerifyError, lib, EXPORTS, LIB_PATH
 from .ops import (abi_version, tree_build, expand_workspace, ExpandOutputs, tree_expand_rerank,
                   attn_workspace, tree_verify_attn, tree_accept, tree_kv_compact,
-                  tree_accept_stochastic, tree_draft_continue, budget_thresholds)
+                  tree_accept_stochastic, tree_draft_continue, tree_candidate_logits,
+                  budget_thresholds)
 
 __all__ = ["TreeVerifyError", "lib", "EXPORTS", "LIB_PATH", "abi_version", "tree_build",
            "expand_workspace", "ExpandOutputs", "tree_expand_rerank", "attn_workspace",
            "tree_verify_attn", "tree_accept", "tree_kv_compact", "tree_accept_stochastic",
-           "tree_draft_continue", "budget_thresholds"]
+           "tree_draft_continue", "tree_candidate_logits", "budget_thresholds"]

@@ -13,7 +13,8 @@ TV_F32, TV_BF16 = 0, 1
 EXPORTS = ("tv_abi_version", "tv_status_string", "tree_build", "tree_expand_workspace_size",
            "tree_expand_rerank", "tree_draft_continue", "tree_budget_thresholds",
            "tree_verify_attn_workspace_size", "tree_verify_attn",
-           "tree_accept", "tree_accept_stochastic", "tree_kv_compact")
+           "tree_accept", "tree_accept_stochastic", "tree_kv_compact",
+           "tree_candidate_workspace_size", "tree_candidate_logits")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -36,6 +37,8 @@ _SIGNATURES = {
     "tree_accept_stochastic": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P]),
     "tree_kv_compact": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
+    "tree_candidate_workspace_size": (_S, [_I, _I]),
+    "tree_candidate_logits": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
 }
 
 _lib = None

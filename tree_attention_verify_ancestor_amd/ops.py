@@ -122,6 +122,32 @@ def tree_draft_continue(ws, B, k, max_steps, m=0, m_per_seq=None, budget_log=Non
     return more
 
 
+def tree_candidate_logits(h, A, Bm, W, C, logits=None, cand=None, ws=None):
+    """The low-rank candidate head: bf16 h [rows][d], A [r][d], Bm [vocab][r], W [vocab][d]
+    -> (fp32 logits [rows][vocab], int32 candidates [rows][C])."""
+    _need(h, "h", torch.bfloat16, 2)
+    rows, d = h.shape
+    _need(A, "A", torch.bfloat16, 2)
+    r = A.shape[0]
+    _need(Bm, "Bm", torch.bfloat16, 2)
+    vocab = Bm.shape[0]
+    _need(W, "W", torch.bfloat16, shape=(vocab, d))
+    if A.shape[1] != d or Bm.shape[1] != r:
+        raise ValueError("A must be [r][d] and Bm [vocab][r]")
+    dev = h.device
+    if logits is None:
+        logits = torch.empty((rows, vocab), dtype=torch.float32, device=dev)
+    if cand is None:
+        cand = torch.empty((rows, C), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty((max(16, lib().tree_candidate_workspace_size(rows, r)),), dtype=torch.uint8,
+                         device=dev)
+    check("tree_candidate_logits", lib().tree_candidate_logits(
+        rows, d, r, vocab, C, _ptr(h), _ptr(A), _ptr(Bm), _ptr(W), _ptr(logits), _ptr(cand),
+        _ptr(ws), ws.numel(), _stream()))
+    return logits, cand
+
+
 def budget_thresholds(cost_us, threshold):
     """Per-place bars of the verify budget from a cost table: cost_us[N-1] = latency of
     one tree_verify_attn call with N nodes per tree (N = 1..n_max).  Returns a host
