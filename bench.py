@@ -16,9 +16,10 @@ the tree_verify_attn call: its algorithmic bytes (prefix K/V + tree K/V + Q + O)
 divided by its average duration, measured with HIP events on its stream around
 graph replays of back-to-back attention calls over the rotated copies.  The CPU
 baseline is the plain oracle timed on a bounded sample on the host cores.  The KV
-compaction that follows acceptance (tree_kv_compact) and the rejection-sampling
-acceptance (tree_accept_stochastic, on seeded target/draft distributions) are timed
-the same way, outside the step, and reported beside it.
+compaction that follows acceptance (tree_kv_compact), the rejection-sampling
+acceptance (tree_accept_stochastic, on seeded target/draft distributions) and the
+draft model's low-rank candidate head (tree_candidate_logits, synthetic weights) are
+timed the same way, outside the step, and reported beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -317,9 +318,49 @@ def gpu_leg(args, inp):
         torch.cuda.synchronize()
         stoch = {"us_per_call": a0.elapsed_time(a1) / (args.attn_reps * 4) * 1e3, "vocab": V,
                  "accepted_per_seq": float(s_keep[0][0].float().mean().item())}
+    # the low-rank candidate head (outside the step) at a draft shape: one row per
+    # frontier node (k, or 10 for a static tree), hidden size 4096, rank 256, the
+    # workload's vocabulary (32000 for a static tree), 64 candidates; synthetic bf16
+    # weights, the low-rank factors rotated over >= 512 MiB of copies
+    rows_c = int(w.k) if inp.dynamic else 10
+    Vc = int(w.V) if inp.dynamic else 32000
+    dc, rc, Cc = 4096, 256, 64
+    gen = torch.Generator(device=dev).manual_seed(5)
+    rnd = lambda shape, sc: (torch.randn(shape, generator=gen, device=dev) * sc).to(torch.bfloat16)
+    W_c = rnd((Vc, dc), 2 * dc ** -0.5)
+    per_c = (rc * dc + Vc * rc) * 2
+    n_c = max(2, math.ceil((512 << 20) / per_c))
+    facs = [(rnd((rc, dc), dc ** -0.5), rnd((Vc, rc), 2 * rc ** -0.5)) for _ in range(n_c)]
+    h_c = rnd((rows_c, dc), 1.0)
+    lg_c = torch.empty((rows_c, Vc), dtype=torch.float32, device=dev)
+    cd_c = torch.empty((rows_c, Cc), dtype=torch.int32, device=dev)
+    ws_c = torch.empty((tv.lib().tree_candidate_workspace_size(rows_c, rc),), dtype=torch.uint8, device=dev)
+    run_c = lambda fa: tv.tree_candidate_logits(h_c, fa[0], fa[1], W_c, Cc, logits=lg_c, cand=cd_c, ws=ws_c)
+    with torch.cuda.stream(side):
+        run_c(facs[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        for fa in facs:
+            run_c(fa)
+    cg.replay()
+    torch.cuda.synchronize()
+    a0.record(stream)
+    for _ in range(max(1, args.attn_reps // 4)):
+        cg.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    cand_ms = a0.elapsed_time(a1) / (max(1, args.attn_reps // 4) * n_c)
+    cand_bytes = (rc * dc + Vc * rc + rows_c * dc + rows_c * Cc * dc) * 2 + rows_c * Vc * 4
+    cand = {"us_per_call": cand_ms * 1e3, "rows": rows_c, "hidden": dc, "rank": rc, "vocab": Vc,
+            "candidates": Cc, "bytes_per_call": cand_bytes,
+            "GB/s": cand_bytes / (cand_ms * 1e-3) / 1e9,
+            "full_head_bytes": Vc * dc * 2 + rows_c * dc * 2 + rows_c * Vc * 4}
+    del facs, W_c
     return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, copies=R,
                 tree=tree_host, compact_ms=compact_ms, compact_bytes=compact_bytes,
-                compact_rows=rows_written / R, stochastic=stoch)
+                compact_rows=rows_written / R, stochastic=stoch, candidates=cand)
 
 
 def copy_reference(mib):
@@ -431,6 +472,7 @@ def main():
     }
     if g["stochastic"] is not None:
         line["accept_stochastic"] = g["stochastic"]
+    line["candidate_head"] = g["candidates"]
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_leg(args, inp, g["tree"])
     print(json.dumps(line), flush=True)

@@ -178,7 +178,7 @@ tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int
  * Outputs: logits fp32 [rows][vocab], cand int32 [rows][C].  All device pointers,
  * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r) bytes (z), no
  * initialisation needed.
- * Limits: d % 8 == 0, r % 8 == 0, 8 <= r <= 512, 1 <= C <= 256, C <= vocab.
+ * Limits: d % 8 == 0, r % 32 == 0, 32 <= r <= 512, 1 <= C <= 256, C <= vocab.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED (alignment), TV_ERR_WORKSPACE.
  */
 size_t tree_candidate_workspace_size(int rows, int r);

@@ -109,7 +109,7 @@ def test_candidate_logits_validation(L):
     assert f(h=Z) == NULL
     assert f(rows=0) == SHAPE
     assert f(d=12) == SHAPE
-    assert f(r=12) == SHAPE
+    assert f(r=40) == SHAPE                      # r % 32
     assert f(r=520) == SHAPE
     assert f(C=0) == SHAPE
     assert f(C=257) == SHAPE

@@ -682,8 +682,9 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("seed,rows,d,r,V,C", [(1, 3, 72, 24, 1000, 13), (2, 10, 4096, 256, 32000, 64),
-                                              (3, 40, 512, 128, 5000, 256), (4, 2, 64, 8, 37, 37)])
+@pytest.mark.parametrize("seed,rows,d,r,V,C", [(1, 3, 72, 32, 1000, 13), (2, 10, 4096, 256, 32000, 64),
+                                              (3, 40, 512, 128, 5000, 256), (4, 2, 64, 32, 37, 37),
+                                              (5, 9, 136, 96, 3001, 40)])
 def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
     """Bit-exact logits and candidate lists against the oracle, except entries (and
     lists) the oracle flags as depending on the order of a float64 sum."""
@@ -700,6 +701,24 @@ def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
         if not rcind[i]:
             assert np.array_equal(cd[i], rc[i]), i
     assert not rcind.all()
+
+
+def test_candidate_logits_tied_scores():
+    """Token rows of Bm repeat every 50 tokens, so scores tie across many ids and the
+    C-th place falls inside a tie: candidates must follow the lower id."""
+    hb, Ab, Bb, Wb = _cand_inputs(11, 4, 256, 64, 3000)
+    Bb = np.ascontiguousarray(np.tile(Bb[:50], (60, 1)))
+    f = synth.bf16_to_f32
+    for C in (7, 64, 130):
+        ref, rc, rind, rcind = oracle.candidate_logits(f(hb), f(Ab), f(Bb), f(Wb), C)
+        lg, cd = tv.tree_candidate_logits(_bf16_dev(hb), _bf16_dev(Ab), _bf16_dev(Bb), _bf16_dev(Wb), C)
+        torch.cuda.synchronize()
+        lg, cd = lg.cpu().numpy(), cd.cpu().numpy()
+        ok = ~rind
+        assert np.array_equal(lg.view(np.uint32)[ok], ref.view(np.uint32)[ok])
+        for i in range(4):
+            if not rcind[i]:
+                assert np.array_equal(cd[i], rc[i]), (C, i)
 
 
 def test_candidate_head_feeds_expansion():

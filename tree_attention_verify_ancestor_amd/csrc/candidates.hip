@@ -12,15 +12,17 @@
 // float32) values and rounded once to float32, so the candidate set and every
 // output bit are fixed up to the order of a float64 sum.
 //
-// Three kernels per call:
+// Four kernels per call:
 //   cand_z_kernel      one wave per (row, j): z[row][j], lanes split d, float64 sums
-//   cand_score_kernel  one thread per token, rows in groups of 32 with z in LDS: the
-//                      low-rank scores, written into the logits rows
-//   cand_select_kernel one workgroup per row: the C best scores by radix selection on
-//                      order-preserving keys (ties to the lower id), the candidates
-//                      ranked best first, then one wave per candidate computes its
-//                      exact logit and overwrites the score
-// HBM traffic: Bm (V*r*2 B) once per group of 32 rows, the C rows of W per draft row
+//   cand_score_kernel  four lanes per token (each a quarter of r), rows in groups of 8
+//                      with z in LDS: the low-rank scores, written into the logits rows
+//   cand_select_kernel one workgroup per row: a lower bound on the C-th best score from
+//                      the threads' maxima, the few scores above it gathered in LDS and
+//                      ranked there (ties to the lower id); with heavy ties, radix
+//                      selection over the whole row on order-preserving keys
+//   cand_exact_kernel  one wave per (row, candidate): its exact logit overwrites the
+//                      score
+// HBM traffic: Bm (V*r*2 B) once per group of 8 rows, the C rows of W per draft row
 // (C*d*2 B), A once per row, and the logits rows written then read once.
 #include "tv_internal.h"
 
@@ -28,9 +30,11 @@ namespace tv {
 
 constexpr int kCandMaxC = 256;
 constexpr int kCandMaxR = 512;
-constexpr int kCandGroup = 32;                 // rows per score workgroup
+constexpr int kCandGroup = 8;                  // rows per score workgroup
+constexpr int kCandSplit = 4;                  // lanes per token in the score kernel
 constexpr int kCandSelThreads = 1024;
-constexpr int kCandSelWaves = kCandSelThreads / kWave;
+constexpr int kCandGather = 2048;              // keys above the lower bound ranked in LDS
+constexpr int kCandCache = 32 * 1024;          // vocabularies whose keys stay in LDS
 
 // Order-preserving map of a float to an unsigned key: a larger value has a larger key,
 // -0 and +0 share one key.
@@ -77,118 +81,216 @@ __global__ __launch_bounds__(256) void cand_score_kernel(int rows, int r, int V,
   const int gr = min(kCandGroup, rows - g0);
   for (int t = threadIdx.x; t < gr * r; t += blockDim.x) sz[t] = z[(size_t)g0 * r + t];
   __syncthreads();
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= V) return;
+  const int v = blockIdx.x * (256 / kCandSplit) + threadIdx.x / kCandSplit;
+  const int part = threadIdx.x % kCandSplit;
+  const int rq = r / kCandSplit;                         // a multiple of 8
   double acc[kCandGroup];
 #pragma unroll
   for (int k = 0; k < kCandGroup; ++k) acc[k] = 0.0;
-  const __bf16* bp = Bm + (size_t)v * r;
-  for (int j0 = 0; j0 < r; j0 += 8) {
-    const bf16x8 bv = *(const bf16x8*)(bp + j0);
+  if (v < V) {
+    const __bf16* bp = Bm + (size_t)v * r + part * rq;
+    const float* zp = sz + part * rq;
+    for (int j0 = 0; j0 < rq; j0 += 8) {
+      const bf16x8 bv = *(const bf16x8*)(bp + j0);
 #pragma unroll
-    for (int k = 0; k < kCandGroup; ++k) {
-      if (k < gr) {
+      for (int k = 0; k < kCandGroup; ++k) {
+        if (k < gr) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)                    // bf16 x float32: exact in float64
-          acc[k] = fma((double)(float)bv[e], (double)sz[k * r + j0 + e], acc[k]);
+          for (int e = 0; e < 8; ++e)                  // bf16 x float32: exact in float64
+            acc[k] = fma((double)(float)bv[e], (double)zp[k * r + j0 + e], acc[k]);
+        }
       }
     }
   }
+  // the four quarters of each dot, summed in a fixed order by every lane of the group
 #pragma unroll
-  for (int k = 0; k < kCandGroup; ++k)
-    if (k < gr) logits[(size_t)(g0 + k) * V + v] = (float)acc[k];
+  for (int k = 0; k < kCandGroup; ++k) {
+    acc[k] += __shfl_xor(acc[k], 1);
+    acc[k] += __shfl_xor(acc[k], 2);
+  }
+  if (v < V && part == 0) {
+#pragma unroll
+    for (int k = 0; k < kCandGroup; ++k)
+      if (k < gr) logits[(size_t)(g0 + k) * V + v] = (float)acc[k];
+  }
 }
 
 __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
-    int d, int V, int C, const __bf16* __restrict__ h, const __bf16* __restrict__ W,
-    float* __restrict__ logits, int32_t* __restrict__ cand) {
+    int V, int C, const float* __restrict__ logits, int32_t* __restrict__ cand) {
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  float* lrow = logits + (size_t)row * V;
+  const float* lrow = logits + (size_t)row * V;
   __shared__ uint32_t s_hist[256];
-  __shared__ int s_digit, s_before, s_n;
-  __shared__ int s_wtot[kCandSelWaves];
+  __shared__ int s_digit, s_before, s_n, s_ties, s_cnt;
+  __shared__ uint32_t s_tmax[kCandSelThreads];
+  __shared__ uint32_t s_gk[kCandGather];
+  __shared__ int s_gi[kCandGather];
   __shared__ int s_ids[kCandMaxC];
   __shared__ uint32_t s_keys[kCandMaxC];
   __shared__ int s_rank[kCandMaxC];
+  __shared__ uint32_t s_row[kCandCache];
 
-  // T = the C-th largest key, 8 bits at a time from the top; `need` ends as the number
-  // of entries equal to T that are selected (the lowest ids among them)
-  uint32_t T = 0, tmask = 0;
-  int need = C;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) s_hist[tid] = 0u;
-    __syncthreads();
-    for (int v = tid; v < V; v += kCandSelThreads) {
-      const uint32_t u = cand_key(lrow[v]);
-      if ((u & tmask) == T) atomicAdd(&s_hist[(u >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds digits 255-4l .. 252-4l, scanned from the top
-      uint32_t hv[4], sum = 0;
+  // every pass over the row: eight coalesced key loads per thread in flight, then the
+  // body for each (id, key)
+  constexpr int kBatch = 8;
+  auto for_each_key = [&](auto&& body) {
+    for (int base = 0; base < V; base += kBatch * kCandSelThreads) {
+      uint32_t u[kBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hv[q] = s_hist[255 - 4 * lane - q];
-        sum += hv[q];
+      for (int j = 0; j < kBatch; ++j) {
+        const int v = base + j * kCandSelThreads + tid;
+        u[j] = v < V ? cand_key(lrow[v]) : 0u;
       }
-      uint32_t incl = sum;
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int v = base + j * kCandSelThreads + tid;
+        if (v < V) body(v, u[j]);
       }
-      const uint32_t before = incl - sum;
-      if (before < (uint32_t)need && (uint32_t)need <= incl) {
-        uint32_t cum = before;
-        int dg = 255 - 4 * lane;
+    }
+  };
+  // Radix selection, 8 bits at a time from the top, over the keys each_key visits:
+  // T = the k-th largest key; `need` = how many entries equal to T complete the k.
+  auto radix_select = [&](auto&& each_key, int k, uint32_t& T, int& need) {
+    uint32_t tmask = 0;
+    T = 0;
+    need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) s_hist[tid] = 0u;
+      __syncthreads();
+      each_key([&](int, uint32_t u) {
+        if ((u & tmask) == T) atomicAdd(&s_hist[(u >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds digits 255-4l .. 252-4l, scanned from the top
+        uint32_t hv[4], sum = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (cum + hv[q] >= (uint32_t)need) {
-            dg = 255 - 4 * lane - q;
-            break;
-          }
-          cum += hv[q];
+          hv[q] = s_hist[255 - 4 * lane - q];
+          sum += hv[q];
         }
-        s_digit = dg;
-        s_before = (int)cum;
+        uint32_t incl = sum;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        const uint32_t before = incl - sum;
+        if (before < (uint32_t)need && (uint32_t)need <= incl) {
+          uint32_t cum = before;
+          int dg = 255 - 4 * lane;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (cum + hv[q] >= (uint32_t)need) {
+              dg = 255 - 4 * lane - q;
+              break;
+            }
+            cum += hv[q];
+          }
+          s_digit = dg;
+          s_before = (int)cum;
+        }
       }
+      __syncthreads();
+      T |= (uint32_t)s_digit << shift;
+      tmask |= 255u << shift;
+      need -= s_before;
+      __syncthreads();
+    }
+  };
+
+  // the row's keys stay in LDS when they fit: one pass over global memory, the others
+  // over LDS
+  const bool cached = V <= kCandCache;
+  auto each_key = [&](auto&& body) {
+    if (cached) {
+      for (int v = tid; v < V; v += kCandSelThreads) body(v, s_row[v]);
+    } else {
+      for_each_key(body);
+    }
+  };
+
+  // A lower bound first: each thread's largest key, and T0 the C-th largest of those
+  // (C threads hold a key >= T0, so the C best keys are all >= T0).  The keys >= T0
+  // are usually few: they are gathered in LDS and ranked there.
+  uint32_t tmax = 0;
+  for_each_key([&](int v, uint32_t u) {
+    tmax = max(tmax, u);
+    if (cached) s_row[v] = u;
+  });
+  s_tmax[tid] = tmax;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  uint32_t T0;
+  int need0;
+  radix_select([&](auto&& body) { body(tid, s_tmax[tid]); }, C, T0, need0);
+  int ge = 0;
+  each_key([&](int, uint32_t u) { ge += u >= T0; });
+  if (ge) atomicAdd(&s_cnt, ge);
+  __syncthreads();
+  const int n_ge = s_cnt;
+  if (n_ge <= kCandGather) {
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    each_key([&](int v, uint32_t u) {
+      if (u >= T0) {
+        const int slot = atomicAdd(&s_n, 1);
+        s_gk[slot] = u;
+        s_gi[slot] = v;
+      }
+    });
+    __syncthreads();
+    // rank by (larger key, lower id); the first C are the candidates
+    for (int gi = tid; gi < n_ge; gi += kCandSelThreads) {
+      const uint32_t km = s_gk[gi];
+      const int im = s_gi[gi];
+      int rk = 0;
+      for (int o = 0; o < n_ge; ++o) rk += s_gk[o] > km || (s_gk[o] == km && s_gi[o] < im);
+      if (rk < C) s_rank[rk] = im;
     }
     __syncthreads();
-    T |= (uint32_t)s_digit << shift;
-    tmask |= 255u << shift;
-    need -= s_before;
-    __syncthreads();
+    if (tid < C) cand[(size_t)row * C + tid] = s_rank[tid];
+    return;
   }
 
-  // selected: keys above T, and the `need` lowest ids with key T (each thread scans a
-  // contiguous segment; a block scan of the per-thread tie counts orders the ties)
-  if (tid == 0) s_n = 0;
-  const int seg = (V + kCandSelThreads - 1) / kCandSelThreads;
-  const int cs = tid * seg;
-  int ties = 0;
-  for (int q = 0; q < seg; ++q)
-    if (cs + q < V && cand_key(lrow[cs + q]) == T) ++ties;
-  int incl = ties;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
+  // Many keys >= T0 (heavy ties): the exact selection over the whole row.  Selected:
+  // keys above T, and the `need` lowest ids with key T.  Usually every entry with key
+  // T is taken, so no order among them is needed; otherwise one wave takes them in id
+  // order.
+  uint32_t T;
+  int need;
+  radix_select(for_each_key, C, T, need);
+  if (tid == 0) {
+    s_n = 0;
+    s_ties = 0;
   }
-  if (lane == kWave - 1) s_wtot[wave] = incl;
   __syncthreads();
-  int trank = incl - ties;
-  for (int w = 0; w < wave; ++w) trank += s_wtot[w];
-  for (int q = 0; q < seg; ++q) {
-    const int v = cs + q;
-    if (v >= V) break;
-    const uint32_t u = cand_key(lrow[v]);
-    const bool take = u > T || (u == T && trank < need);
-    if (u == T) ++trank;
-    if (take) {
+  int ties = 0;
+  for_each_key([&](int, uint32_t u) { ties += u == T; });
+  if (ties) atomicAdd(&s_ties, ties);
+  __syncthreads();
+  const bool take_all = s_ties == need;
+  for_each_key([&](int v, uint32_t u) {
+    if (u > T || (take_all && u == T)) {
       const int slot = atomicAdd(&s_n, 1);
       s_ids[slot] = v;
       s_keys[slot] = u;
+    }
+  });
+  if (!take_all && wave == 0) {
+    int taken = 0;
+    for (int base = 0; base < V && taken < need; base += kWave) {
+      const int v = base + lane;
+      const bool t = v < V && cand_key(lrow[v]) == T;
+      const uint64_t bal = __ballot(t);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (t && taken + before < need) {
+        const int slot = atomicAdd(&s_n, 1);
+        s_ids[slot] = v;
+        s_keys[slot] = T;
+      }
+      taken += __popcll(bal);
     }
   }
   __syncthreads();
@@ -202,12 +304,22 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   }
   __syncthreads();
   if (tid < C) cand[(size_t)row * C + tid] = s_rank[tid];
-  // exact logits of the candidates (every read of the scores is done)
-  for (int c = wave; c < C; c += kCandSelWaves) {
-    const int v = s_rank[c];
-    const double s = wave_dot_bf16(W + (size_t)v * d, h + (size_t)row * d, d, lane);
-    if (lane == 0) lrow[v] = (float)s;
-  }
+}
+
+// The exact logit of each candidate, one wave per (row, candidate).
+__global__ __launch_bounds__(256) void cand_exact_kernel(int d, int V, int C,
+                                                        const __bf16* __restrict__ h,
+                                                        const __bf16* __restrict__ W,
+                                                        const int32_t* __restrict__ cand,
+                                                        float* __restrict__ logits) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = blockIdx.x * 4 + wave;
+  const int row = blockIdx.y;
+  if (c >= C) return;                                          // wave-uniform
+  const int v = cand[(size_t)row * C + c];
+  const double s = wave_dot_bf16(W + (size_t)v * d, h + (size_t)row * d, d, lane);
+  if (lane == 0) logits[(size_t)row * V + v] = (float)s;
 }
 
 }  // namespace tv
@@ -222,7 +334,7 @@ TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C,
                                        float* logits, int32_t* cand, void* ws, size_t ws_bytes,
                                        hipStream_t stream) {
   if (!h || !A || !Bm || !W || !logits || !cand) return TV_ERR_NULL;
-  if (rows < 1 || d < 8 || d % 8 != 0 || r < 8 || r % 8 != 0 || r > tv::kCandMaxR ||
+  if (rows < 1 || d < 8 || d % 8 != 0 || r < 32 || r % 32 != 0 || r > tv::kCandMaxR ||
       C < 1 || C > tv::kCandMaxC || vocab < C)
     return TV_ERR_SHAPE;
   if ((((uintptr_t)h | (uintptr_t)A | (uintptr_t)Bm | (uintptr_t)W) & 15) != 0)
@@ -232,10 +344,14 @@ TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C,
   float* z = (float*)ws;
   hipLaunchKernelGGL(tv::cand_z_kernel, dim3((r + 3) / 4, rows), dim3(256), 0, stream, d, r,
                      (const __bf16*)h, (const __bf16*)A, z);
+  constexpr int kTokensPerWg = 256 / tv::kCandSplit;
   hipLaunchKernelGGL(tv::cand_score_kernel,
-                     dim3((vocab + 255) / 256, (rows + tv::kCandGroup - 1) / tv::kCandGroup),
+                     dim3((vocab + kTokensPerWg - 1) / kTokensPerWg,
+                          (rows + tv::kCandGroup - 1) / tv::kCandGroup),
                      dim3(256), 0, stream, rows, r, vocab, (const __bf16*)Bm, (const float*)z, logits);
-  hipLaunchKernelGGL(tv::cand_select_kernel, dim3(rows), dim3(tv::kCandSelThreads), 0, stream, d,
-                     vocab, C, (const __bf16*)h, (const __bf16*)W, logits, cand);
+  hipLaunchKernelGGL(tv::cand_select_kernel, dim3(rows), dim3(tv::kCandSelThreads), 0, stream,
+                     vocab, C, (const float*)logits, cand);
+  hipLaunchKernelGGL(tv::cand_exact_kernel, dim3((C + 3) / 4, rows), dim3(256), 0, stream, d, vocab,
+                     C, (const __bf16*)h, (const __bf16*)W, (const int32_t*)cand, logits);
   return tv::launch_status();
 }
