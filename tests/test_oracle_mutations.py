@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.accept
 import oracle.attention
+import oracle.candidates
 import oracle.compact
 import oracle.stochastic
 import oracle.expand
@@ -104,6 +105,15 @@ MUTATIONS = {
         (oracle.expand, "best_child_kept", lambda place, m, run: place < m - 1 and run == place)],
     "stop: the verify budget ignored": [
         (oracle.expand, "best_child_kept", lambda place, m, run: place <= m - 1)],
+    "candidates: ties to the higher id": [
+        (oracle.candidates, "top_candidates",
+         lambda s, C: (len(s) - 1 - np.argsort(-np.asarray(s, np.float32)[::-1], kind="stable"))[:C])],
+    "candidates: dot products summed in float32": [
+        (oracle.candidates, "dot_rows",
+         lambda M, x: (np.asarray(M, np.float32) @ np.asarray(x, np.float32)).astype(np.float64))],
+    "candidates: lowest scores selected": [
+        (oracle.candidates, "top_candidates",
+         lambda s, C: np.argsort(np.asarray(s, np.float32), kind="stable")[:C])],
     "compact: one node short": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }
