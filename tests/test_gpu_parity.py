@@ -684,7 +684,9 @@ def _bf16_dev(bits):
 
 @pytest.mark.parametrize("seed,rows,d,r,V,C", [(1, 3, 72, 32, 1000, 13), (2, 10, 4096, 256, 32000, 64),
                                               (3, 40, 512, 128, 5000, 256), (4, 2, 64, 32, 37, 37),
-                                              (5, 9, 136, 96, 3001, 40)])
+                                              (5, 9, 136, 96, 3001, 40),
+                                              # scores past the LDS cache (a 128256-token vocabulary)
+                                              (6, 4, 256, 64, 128256, 64)])
 def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
     """Bit-exact logits and candidate lists against the oracle, except entries (and
     lists) the oracle flags as depending on the order of a float64 sum."""
@@ -703,11 +705,13 @@ def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
     assert not rcind.all()
 
 
-def test_candidate_logits_tied_scores():
+@pytest.mark.parametrize("V", [3000, 40000])
+def test_candidate_logits_tied_scores(V):
     """Token rows of Bm repeat every 50 tokens, so scores tie across many ids and the
-    C-th place falls inside a tie: candidates must follow the lower id."""
-    hb, Ab, Bb, Wb = _cand_inputs(11, 4, 256, 64, 3000)
-    Bb = np.ascontiguousarray(np.tile(Bb[:50], (60, 1)))
+    C-th place falls inside a tie: candidates must follow the lower id (in LDS and,
+    past its cache, over the whole row)."""
+    hb, Ab, Bb, Wb = _cand_inputs(11, 4, 256, 64, V)
+    Bb = np.ascontiguousarray(np.tile(Bb[:50], (V // 50, 1)))
     f = synth.bf16_to_f32
     for C in (7, 64, 130):
         ref, rc, rind, rcind = oracle.candidate_logits(f(hb), f(Ab), f(Bb), f(Wb), C)
