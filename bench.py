@@ -433,8 +433,8 @@ def _cpu_steps(args, inp, oracle, synth, blas):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path does "
-              f"not shard across GPUs in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library "
+              f"runs on one GPU and does not shard across GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_mib > 0:
         copy_reference(args.copy_mib)
