@@ -51,7 +51,7 @@ typedef enum {
   TV_ERR_NULL = 1,         /* a required pointer is NULL */
   TV_ERR_SHAPE = 2,        /* a size argument is out of range or inconsistent */
   TV_ERR_DTYPE = 3,        /* unknown tv_dtype */
-  TV_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement (e.g. head_dim) */
+  TV_ERR_UNSUPPORTED = 4,  /* valid request the library does not implement (e.g. head_dim) */
   TV_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the size query returns */
   TV_ERR_HIP = 6           /* the HIP runtime reported an error when launching */
 } tv_status;

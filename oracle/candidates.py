@@ -4,7 +4,7 @@
 head first scores the vocabulary in a smaller representation and then computes full
 logits only for the selected candidates, to cut the cost of next-token prediction.
 
-Readings taken where the page leaves a step open (each is listed in the design doc):
+Readings taken where the page leaves a step open:
 * The smaller representation is a rank-r factorisation of the LM head: z = A h
   (A: [r][d]) and a low-rank score s_v = Bm[v] . z for every token (Bm: [V][r]); the
   full logit is l_v = W[v] . h (W: [V][d]).  h, A, Bm, W are bf16.

@@ -9,7 +9,7 @@
 * section "Reranking Nodes": after expanding, keep the m nodes of largest global
   acceptance over all nodes generated.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 * Values are ranked through their logarithm (log is monotone): a node's score is
   the sum of the log-confidences on its path.  The log-sum-exp of a logit row is
   computed in float64 (max-shifted), rounded once to float32; a child's score is
@@ -172,9 +172,9 @@ def draft_continue(logits_steps, k, m, budget_log=None, n_max=64):
     probability per unit of measured marginal verification cost decides whether the
     tree is drafted further; drafting stops once it falls below the threshold.
 
-    Reading (listed in the design doc): after level s, let c be the best child that level
-    created (its frontier node of rank 0) and p its place in the whole pool ranked
-    best first by (score descending, creation ascending).  Drafting goes on when c
+    Reading: after level s, let c be the best child that level created (its
+    frontier node of rank 0) and p its place in the whole pool ranked best first by
+    (score descending, creation ascending).  Drafting goes on when c
     would be kept by the final rerank if drafting stopped now: p <= m - 1 and the
     places 1..p all pass the verify budget (budget_cut).  A deeper node scores no
     better than its parent and is created after it, so it ranks after c; when c is
