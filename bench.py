@@ -252,6 +252,15 @@ def gpu_leg(args, inp):
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / (args.attn_reps * R)
+    # the spread over replays: each replay timed on its own (R back-to-back calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.attn_reps + 1)]
+    ev[0].record(stream)
+    for i in range(args.attn_reps):
+        ag.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([ev[i].elapsed_time(ev[i + 1]) / R for i in range(args.attn_reps)])
+    attn_pct = {q: float(np.percentile(per_call, p)) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
 
     # KV compaction after acceptance (outside the step): each copy's accepted
     # continuation into a destination cache, launches back to back
@@ -358,7 +367,8 @@ def gpu_leg(args, inp):
             "GB/s": cand_bytes / (cand_ms * 1e-3) / 1e9,
             "full_head_bytes": Vc * dc * 2 + rows_c * dc * 2 + rows_c * Vc * 4}
     del facs, W_c
-    return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, copies=R,
+    return dict(step_ms=step_ms_events, step_ms_wall=step_ms_wall, attn_ms=attn_ms, attn_pct=attn_pct,
+                copies=R,
                 tree=tree_host, compact_ms=compact_ms, compact_bytes=compact_bytes,
                 compact_rows=rows_written / R, stochastic=stoch, candidates=cand)
 
@@ -464,6 +474,7 @@ def main():
                      "kernel": ("tree_verify_attn (attn_bf16 + attn_combine when split)"
                                 if w.dtype == "bf16" else "tree_verify_attn (attn_f32)"),
                      "bytes_per_launch": abytes, "launch_ms": g["attn_ms"],
+                     "launch_ms_p10_p50_p90": [g["attn_pct"][q] for q in ("p10", "p50", "p90")],
                      "mfma_tflops": mfma_tflops, "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},
         "ms_per_step_wall": g["step_ms_wall"],
         "kv_compact": {"us_per_call": g["compact_ms"] * 1e3, "rows_per_call": g["compact_rows"],
