@@ -86,7 +86,11 @@ __host__ __device__ constexpr int n_buffers(int D, int wk) {
 // tiles of 32 rows (rows = node * G + head within the group).  Small row counts use
 // four waves that split the keys; from 128 rows on, eight waves of one tile each, two
 // per SIMD, so that one wave's softmax runs on the vector ALUs while the other's
-// products occupy the matrix core.
+// products occupy the matrix core.  When 256-row units are few (one or two sequences
+// with many rows), filling the chip would take so many key chunks that the fp32
+// partials outweigh the K/V they summarise; those batches use 64-row units instead
+// (the row blocks of one KV head re-read its keys from L2) and one workgroup per CU,
+// which quarters the chunk count.
 static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_prefix) {
   AttnPlan p{};
   const int G = Hq / Hkv;
@@ -95,13 +99,16 @@ static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_pref
   else if (R <= 64) { p.wq = 1; p.wk = 4; p.qt = 2; }
   else if (R <= 128) { p.wq = 4; p.wk = 2; p.qt = 1; }
   else { p.wq = 8; p.wk = 1; p.qt = 1; }
+  const bool split_rows = R > 128 && (long)B * Hkv * ((R + 255) / 256) < 32;
+  if (split_rows) { p.wq = 1; p.wk = 4; p.qt = 2; }
   p.waves = p.wq * p.wk;
   p.rows_per_wg = 32 * p.qt * p.wq;
   p.n_rb = (R + p.rows_per_wg - 1) / p.rows_per_wg;
   const int kt = stage_keys(p.wk);
   p.units = B * Hkv * p.n_rb;
-  // about two workgroups per CU over 256 CUs; every chunk at least two stages
-  const long target = 512;
+  // about two workgroups per CU over 256 CUs (one for split rows); every chunk at
+  // least two stages
+  const long target = split_rows ? 256 : 512;
   long want = (target + p.units - 1) / p.units;
   if (want < 1) want = 1;
   long ck = (max_prefix + want - 1) / want;
