@@ -30,6 +30,7 @@ namespace tv {
 
 constexpr int kTopKMax = 16;
 constexpr int kPoolMax = 4096;
+static_assert(kPoolMax <= 4096, "pool slots fit 12 bits (depth-order keys) and a short");
 constexpr int kChunkThreads = 256;
 constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kMaxRowChunks = 64;        // chunks per logit row (one lane each when merging)
@@ -52,7 +53,8 @@ struct SeqHeader {
   int32_t count;
   int32_t next_step;
   int32_t pad[13];
-  int32_t frontier[kTopKMax];
+  int32_t frontier[kTopKMax];          // pool slots of the frontier, best first
+  float frontier_score[kTopKMax];      // and their scores (read without a pool lookup)
 };
 
 // What one workgroup of expand_rows_kernel learns about its chunk of a logit row.
@@ -305,6 +307,10 @@ __global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
 __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
 }
+// better() as 0/1 without short-circuit branches, for unrolled counting loops
+__device__ __forceinline__ int beats(float sa, int ia, float sb, int ib) {
+  return (int)(sa > sb) | ((int)(sa == sb) & (int)(ia < ib));
+}
 
 __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     char* __restrict__ ws, size_t stride, size_t rec_off, int k, int step, int rows, int nch,
@@ -322,10 +328,13 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   PoolEntry* pool = (PoolEntry*)(seq + sizeof(SeqHeader));
   const ChunkRec* recs = (const ChunkRec*)(seq + rec_off);
 
-  __shared__ float s_score[kTopKMax * kTopKMax];
+  __shared__ __align__(16) float s_score[kTopKMax * kTopKMax];   // read as float4 when ranking
   __shared__ uint32_t s_key[kPoolMax];
   __shared__ uint8_t s_dep[kPoolMax];
   __shared__ short s_pos[kPoolMax];
+  __shared__ short s_par[kPoolMax];
+  __shared__ int s_ptok[kPoolMax];
+  __shared__ float s_psc[kPoolMax];
   __shared__ uint32_t s_hist[256];
   __shared__ int s_wtot[kSelWaves];
   __shared__ int s_sel_digit, s_sel_before;
@@ -334,6 +343,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   __shared__ int s_kept[TV_MAX_NODES];
   __shared__ int s_kdep[TV_MAX_NODES];
   __shared__ int s_byrank[TV_MAX_NODES];
+  __shared__ uint32_t s_kkey[TV_MAX_NODES];
   __shared__ int s_nkept, s_cut;
   __shared__ int s_status;
   __shared__ int s_m;
@@ -357,6 +367,8 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     s_rowbad = 0;
   }
   if (tid < kTopKMax) s_front[tid] = -1;
+  const int added16 = (added + 15) & ~15;
+  if (tid >= added && tid < added16) s_score[tid] = -INFINITY;   // ranks after every child
   const int rr = wave;
   const bool merger = rr < rows;
   const bool has = merger && lane < nch;
@@ -382,10 +394,11 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
       hi[j] = has && j < k ? rec->id[j] : INT32_MAX;
     }
     if (step > 1) {
+      // the frontier holds the previous level's children: depth step - 1
       pslot = hdr->frontier[rr];
       pslot = pslot < 0 ? 0 : (pslot >= base ? base - 1 : pslot);
-      pscore = pool[pslot].score;
-      pdepth = pool[pslot].depth;
+      pscore = hdr->frontier_score[rr];
+      pdepth = step - 1;
     }
   }
   __syncthreads();
@@ -438,12 +451,21 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     for (int c = tid; c < added; c += kSelThreads) {
       const float sc = s_score[c];
       int rank = 0;
-      for (int o = 0; o < added; ++o) rank += better(s_score[o], o, sc, c);
+      for (int o = 0; o < added16; o += 16) {
+        float4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = *(const float4*)&s_score[o + 4 * j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rank += beats(v[j].x, o + 4 * j, sc, c) + beats(v[j].y, o + 4 * j + 1, sc, c) +
+                  beats(v[j].z, o + 4 * j + 2, sc, c) + beats(v[j].w, o + 4 * j + 3, sc, c);
+      }
       if (rank < k) s_front[rank] = c;
     }
     __syncthreads();
     if (tid < k) {
       hdr->frontier[tid] = base + s_front[tid];
+      hdr->frontier_score[tid] = s_score[s_front[tid]];
       if (frontier_token) frontier_token[(size_t)b * k + tid] = s_tok[s_front[tid]];
     }
   } else if (frontier_token && tid < k) {
@@ -461,6 +483,9 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
         s_key[c] = fkey(e.score);
         s_dep[c] = (uint8_t)e.depth;
         s_pos[c] = -1;
+        s_par[c] = (short)e.parent_slot;
+        s_ptok[c] = e.token;
+        s_psc[c] = e.score;
       }
       __syncthreads();
       if (keep == count) {                               // everything is kept
@@ -545,47 +570,47 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
       // leading run of places j whose score exceeds budget_log[j] stays
       if (budget_log && keep > 0) {
         if (tid == 0) s_cut = keep;
+        if (tid < keep) s_kkey[tid] = s_key[s_kept[tid]];
         __syncthreads();
         if (tid < keep) {
           const int me = s_kept[tid];
-          const uint32_t km = s_key[me];
+          const uint32_t km = s_kkey[tid];
           int r = 0;
+#pragma unroll 8
           for (int o = 0; o < keep; ++o) {
             const int other = s_kept[o];
-            const uint32_t ko = s_key[other];
+            const uint32_t ko = s_kkey[o];
             r += (ko > km) || (ko == km && other < me);
           }
           s_byrank[r] = me;
-          if (!(pool[me].score > budget_log[r + 1])) atomicMin(&s_cut, r);
+          if (!(s_psc[me] > budget_log[r + 1])) atomicMin(&s_cut, r);
         }
         __syncthreads();
         keep = s_cut;
         if (tid < keep) s_kept[tid] = s_byrank[tid];
         __syncthreads();
       }
-      if (tid < keep) s_kdep[tid] = s_dep[s_kept[tid]];
+      // depth above the creation index (< kPoolMax = 2^12): one key orders by both
+      if (tid < keep) s_kdep[tid] = ((int)s_dep[s_kept[tid]] << 12) | s_kept[tid];
       __syncthreads();
       // output position: root first, then by (depth, creation)
       if (tid < keep) {
         const int me = s_kept[tid];
-        const int dme = s_kdep[tid];
+        const int kme = s_kdep[tid];
         int before = 0;
-        for (int o = 0; o < keep; ++o) {
-          const int other = s_kept[o];
-          const int dot = s_kdep[o];
-          before += (dot < dme) || (dot == dme && other < me);
-        }
+#pragma unroll 8
+        for (int o = 0; o < keep; ++o) before += s_kdep[o] < kme;
         s_pos[me] = (short)(1 + before);
       }
       __syncthreads();
       if (tid < keep) {
         const int me = s_kept[tid];
         const int pos = s_pos[me];
-        const PoolEntry e = pool[me];
+        const int ps = s_par[me];
         const size_t o = (size_t)b * n_max + pos;
-        parent[o] = e.parent_slot < 0 ? 0 : s_pos[e.parent_slot];
-        token[o] = e.token;
-        score[o] = e.score;
+        parent[o] = ps < 0 ? 0 : s_pos[ps];
+        token[o] = s_ptok[me];
+        score[o] = s_psc[me];
       }
     }
     const int n = (st == TV_SEQ_OK) ? keep + 1 : 0;
