@@ -23,13 +23,15 @@
 //     2^48) and accumulates O^T += V^T P^T, reading V^T with ds_read_b64_tr_b16.
 //     Shapes: up to 32 rows, 4 waves split each stage's keys; up to 64 rows, the same
 //     with two row tiles per wave; up to 128 rows, 8 waves as 4 row groups x 2 key
-//     halves; beyond, 8 waves of one 32-row tile each.  With 8 waves two share each
-//     SIMD, so one wave's softmax (vector ALUs) runs beside the other's products.
+//     halves; beyond, 8 waves of one 32-row tile each (or 64-row units of the second
+//     shape when such 256-row units are few).  With 8 waves two share each SIMD, so
+//     one wave's softmax (vector ALUs) runs beside the other's products.
 //     Key-split waves merge their (m, l, O) through LDS.  The output per row and chunk
 //     is the final bf16 row when one chunk covers the prefix, else an unnormalised
 //     fp32 partial plus (m, l).
-//   attn_combine   sixteen lanes per output row merge the chunk partials (eight chunks
-//     in flight at a time), write bf16 out and the natural-log lse.
+//   attn_combine   sixteen lanes per output row, four or eight rows per workgroup,
+//     merge the chunk partials (eight chunks in flight at a time), write bf16 out and
+//     the natural-log lse.
 // fp32 path: attn_f32, one workgroup per output row on the vector ALUs (the
 // fp32 workloads are small correctness cases).
 #include <math.h>
@@ -836,18 +838,20 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 
 // Merge of the key-chunk partials for the rows whose sequence spans more than one
 // chunk (the others were written by attn_bf16).  Sixteen lanes per output row, four
-// rows per wave, sixteen per workgroup: a lane owns D/16 consecutive dims (16-byte
+// rows per wave, CR rows per workgroup: a lane owns D/16 consecutive dims (16-byte
 // loads and one 8- or 16-byte store).  The partials are loaded eight chunks at a time
-// before any is used and merged online against a running maximum.
+// before any is used and merged online against a running maximum.  Few output rows
+// (one sequence) take four rows per workgroup, so that the live rows spread over
+// more CUs; many take eight.
 constexpr int kCombineLanes = 16;                    // lanes per output row
-constexpr int kCombineRows = 256 / kCombineLanes;    // output rows per workgroup
 constexpr int kCombineBatch = 8;                     // chunk partials in flight per lane
+constexpr int kCombineFewRows = 4096;                // up to this many: four rows per workgroup
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+template <int D, int CR>
+__global__ __launch_bounds__(kCombineLanes * CR) void attn_combine(AttnArgs a) {
   constexpr int DPL = D / kCombineLanes;             // dims per lane: 8 or 4
   constexpr int V4 = DPL / 4;                        // f32x4 loads per lane and chunk
-  const int row = blockIdx.x * kCombineRows + threadIdx.x / kCombineLanes;
+  const int row = blockIdx.x * CR + threadIdx.x / kCombineLanes;
   if (row >= a.B * a.n_max * a.Hq) return;
   const int d0 = (threadIdx.x % kCombineLanes) * DPL;
   const int h = row % a.Hq;
@@ -1013,8 +1017,10 @@ static void launch_bf16(const AttnPlan& p, const AttnArgs& a, hipStream_t stream
   else hipLaunchKernelGGL((attn_bf16<D, 8, 1, 1>), grid, block, 0, stream, a);
   if (p.n_chunks > 1) {
     const int rows = a.B * a.n_max * a.Hq;
-    hipLaunchKernelGGL(attn_combine<D>, dim3((rows + kCombineRows - 1) / kCombineRows), dim3(256), 0,
-                       stream, a);
+    if (rows <= kCombineFewRows)
+      hipLaunchKernelGGL((attn_combine<D, 4>), dim3((rows + 3) / 4), dim3(kCombineLanes * 4), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_combine<D, 8>), dim3((rows + 7) / 8), dim3(kCombineLanes * 8), 0, stream, a);
   }
 }
 
