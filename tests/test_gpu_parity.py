@@ -200,6 +200,8 @@ SMALL_ATTN = [  # (B, Hq, Hkv, D, prefix lengths, node counts)
     # 65..128 rows per KV head (eight waves as four row groups x two key halves)
     (2, 4, 2, 64, (300, 1000), (64, 40)),
     (1, 6, 3, 128, (777,), (50,)),
+    # one sequence with 240 rows per KV head: 64-row units, one workgroup per CU
+    (1, 32, 8, 128, (3000,), (60,)),
     # eight or more sequences: ragged ones take their (sequence, chunk) pairs by work
     (9, 8, 2, 128, (3000, 17, 0, 900, 2500, 64, 1200, 5, 640), (64, 3, 20, 64, 1, 33, 50, 64, 10)),
     (12, 16, 4, 64, (100, 2000, 50, 700, 1, 0, 3000, 256, 128, 900, 1500, 30),
