@@ -19,9 +19,9 @@
 //                        children are ranked into the next frontier, and on the last
 //                        level the whole pool is ranked, the best m-1 kept and the tree
 //                        written in (depth, creation) order with remapped parents.
-// Workspace per sequence: a header {status, pool count, next step, frontier}, the pool
-// of {parent slot, token, score, depth} records in creation order, then one record
-// per (frontier row, chunk).
+// Workspace per sequence: a header {status, pool count, next step, frontier slots and
+// scores}, the pool of {parent slot, token, score, depth} records in creation order,
+// then one record per (frontier row, chunk).
 #include <math.h>
 
 #include "tv_internal.h"
