@@ -260,7 +260,8 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       for (int j = threadIdx.x; j < P; j += blockDim.x) {
         const int wj = s_work[j];
         int r = 0;
-        for (int i = 0; i < P; ++i) r += s_work[i] > wj || (s_work[i] == wj && i < j);
+        for (int i = 0; i < P; ++i)                  // branch-free: no exec-mask jumps
+          r += (int)(s_work[i] > wj) | ((int)(s_work[i] == wj) & (int)(i < j));
         if (r == place) *s_pick = j;
       }
       __syncthreads();

@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
       const uint32_t km = s_gk[gi];
       const int im = s_gi[gi];
       int rk = 0;
-      for (int o = 0; o < n_ge; ++o) rk += s_gk[o] > km || (s_gk[o] == km && s_gi[o] < im);
+      for (int o = 0; o < n_ge; ++o)                 // branch-free: no exec-mask jumps
+        rk += (int)(s_gk[o] > km) | ((int)(s_gk[o] == km) & (int)(s_gi[o] < im));
       if (rk < C) s_rank[rk] = im;
     }
     __syncthreads();
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
     const uint32_t km = s_keys[tid];
     const int im = s_ids[tid];
     int rk = 0;
-    for (int o = 0; o < C; ++o) rk += s_keys[o] > km || (s_keys[o] == km && s_ids[o] < im);
+    for (int o = 0; o < C; ++o)
+      rk += (int)(s_keys[o] > km) | ((int)(s_keys[o] == km) & (int)(s_ids[o] < im));
     s_rank[rk] = im;
   }
   __syncthreads();

@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
           for (int o = 0; o < keep; ++o) {
             const int other = s_kept[o];
             const uint32_t ko = s_kkey[o];
-            r += (ko > km) || (ko == km && other < me);
+            r += (int)(ko > km) | ((int)(ko == km) & (int)(other < me));
           }
           s_byrank[r] = me;
           if (!(s_psc[me] > budget_log[r + 1])) atomicMin(&s_cut, r);
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_continue_kernel(
   __syncthreads();
   const float ss = s_sc[cs];
   int ahead = 0;
-  for (int c = tid; c < count; c += kSelThreads) ahead += better(s_sc[c], c, ss, cs);
+  for (int c = tid; c < count; c += kSelThreads) ahead += beats(s_sc[c], c, ss, cs);
   if (ahead) atomicAdd(&s_place, ahead);
   __syncthreads();
   const int place = s_place;
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_continue_kernel(
       const float sc = s_sc[c];
       if (c != cs && !better(sc, c, ss, cs)) continue;
       int r = 0;
-      for (int o = 0; o < count; ++o) r += better(s_sc[o], o, sc, c);
+      for (int o = 0; o < count; ++o) r += beats(s_sc[o], o, sc, c);
       if (!(sc > budget_log[r + 1])) s_fail = 1;
     }
     __syncthreads();
