@@ -142,9 +142,10 @@ __device__ __forceinline__ void best_two(const float (&x)[EPT], float after_v, i
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const float v = x[j];
-    const bool after = v < after_v || (v == after_v && j > after_j);
-    const bool c1 = after && v > v1;
-    const bool c2 = after && v > v2;
+    // bitwise, not short-circuit: the compiler would branch around every element
+    const bool after = (v < after_v) | ((v == after_v) & (j > after_j));
+    const bool c1 = after & (v > v1);
+    const bool c2 = after & (v > v2);
     v2 = c1 ? v1 : (c2 ? v : v2);
     j2 = c1 ? j1 : (c2 ? j : j2);
     v1 = c1 ? v : v1;
