@@ -132,16 +132,21 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   __shared__ int s_rank[kCandMaxC];
   __shared__ uint32_t s_row[kCandCache];
 
-  // every pass over the row: eight coalesced key loads per thread in flight, then the
+  // every pass over the row: 32 coalesced key loads per thread in flight, then the
   // body for each (id, key)
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 32;
   auto for_each_key = [&](auto&& body) {
     for (int base = 0; base < V; base += kBatch * kCandSelThreads) {
+      // unconditional loads from clamped addresses, then the select: a load under a
+      // condition is compiled into a branch that waits for it before the next one
+      float x[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) x[j] = lrow[min(base + j * kCandSelThreads + tid, V - 1)];
       uint32_t u[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int v = base + j * kCandSelThreads + tid;
-        u[j] = v < V ? cand_key(lrow[v]) : 0u;
+        u[j] = v < V ? cand_key(x[j]) : 0u;
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
