@@ -26,6 +26,7 @@
 namespace tv {
 
 constexpr int kStochThreads = 1024;
+constexpr int kStochBatch = 8;                // vocabulary loads in flight per thread
 constexpr int kStochMaxVocab = 36864;                    // r in LDS: 144 KB
 
 __device__ __forceinline__ double block_sum_f64(double v, double* sred) {
@@ -67,14 +68,25 @@ __global__ __launch_bounds__(kStochThreads) void accept_stochastic_kernel(
     if (path && tid < n_max) path[row + tid] = -1;
     return;
   }
+  // A thread's elements v = tid + i * kStochThreads are loaded kStochBatch at a time
+  // from clamped addresses before any is used (a load used at once waits a full
+  // memory round trip per element), then taken in increasing v as before.
   // r <- node u's target row; returns its sum
   auto load_row = [&](int u) {
     const float* pr = p_target + (row + u) * V;
     double s = 0.0;
-    for (int v = tid; v < V; v += kStochThreads) {
-      const float x = pr[v];
-      sr[v] = x;
-      s += (double)x;
+    for (int v0 = tid; v0 < V; v0 += kStochBatch * kStochThreads) {
+      float x[kStochBatch];
+#pragma unroll
+      for (int i = 0; i < kStochBatch; ++i) x[i] = pr[min(v0 + i * kStochThreads, V - 1)];
+#pragma unroll
+      for (int i = 0; i < kStochBatch; ++i) {
+        const int v = v0 + i * kStochThreads;
+        if (v < V) {
+          sr[v] = x[i];
+          s += (double)x[i];
+        }
+      }
     }
     return block_sum_f64(s, sred);                          // its barrier publishes sr
   };
@@ -114,12 +126,21 @@ __global__ __launch_bounds__(kStochThreads) void accept_stochastic_kernel(
       __syncthreads();                                      // every thread has read sr[x]
       const float S32 = (float)S;
       double s = 0.0;
-      for (int v = tid; v < V; v += kStochThreads) {
+      for (int v0 = tid; v0 < V; v0 += kStochBatch * kStochThreads) {
+        float qv[kStochBatch];
+#pragma unroll
+        for (int i = 0; i < kStochBatch; ++i) qv[i] = q[min(v0 + i * kStochThreads, V - 1)];
+#pragma unroll
+        for (int i = 0; i < kStochBatch; ++i) {
 #pragma clang fp contract(off)
-        const float prod = S32 * q[v];
-        const float nr = fmaxf(sr[v] - prod, 0.f);
-        sr[v] = nr;
-        s += (double)nr;
+          const int v = v0 + i * kStochThreads;
+          if (v < V) {
+            const float prod = S32 * qv[i];
+            const float nr = fmaxf(sr[v] - prod, 0.f);
+            sr[v] = nr;
+            s += (double)nr;
+          }
+        }
       }
       S = block_sum_f64(s, sred);
     }
