@@ -32,6 +32,7 @@ constexpr int kCandMaxC = 256;
 constexpr int kCandMaxR = 512;
 constexpr int kCandGroup = 8;                  // rows per score workgroup
 constexpr int kCandSplit = 4;                  // lanes per token in the score kernel
+constexpr int kScoreBatch = 8;                 // Bm loads in flight per score thread
 constexpr int kCandSelThreads = 1024;
 constexpr int kCandGather = 2048;              // keys above the lower bound ranked in LDS
 constexpr int kCandCache = 32 * 1024;          // vocabularies whose keys stay in LDS
@@ -50,13 +51,26 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 // Sum over i of a[i] * b[i] for bf16 vectors of length d (d % 8 == 0) by one wave, in
 // float64 (each product of two bf16 values is exact in float32); every lane returns it.
+// A lane's 16-byte pieces are loaded kDotBatch at a time from clamped addresses
+// before any is used, then summed in increasing i as one at a time would be.
+constexpr int kDotBatch = 8;
 __device__ __forceinline__ double wave_dot_bf16(const __bf16* a, const __bf16* b, int d, int lane) {
   double acc = 0.0;
-  for (int i = lane * 8; i < d; i += kWave * 8) {
-    const bf16x8 av = *(const bf16x8*)(a + i);
-    const bf16x8 bv = *(const bf16x8*)(b + i);
+  for (int i0 = lane * 8; i0 < d; i0 += kDotBatch * kWave * 8) {
+    bf16x8 av[kDotBatch], bv[kDotBatch];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (double)((float)av[e] * (float)bv[e]);
+    for (int q = 0; q < kDotBatch; ++q) {
+      const int i = min(i0 + q * kWave * 8, d - 8);
+      av[q] = *(const bf16x8*)(a + i);
+      bv[q] = *(const bf16x8*)(b + i);
+    }
+#pragma unroll
+    for (int q = 0; q < kDotBatch; ++q) {
+      if (i0 + q * kWave * 8 < d) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (double)((float)av[q][e] * (float)bv[q][e]);
+      }
+    }
   }
   return wave_sum_d(acc);
 }
@@ -87,17 +101,27 @@ __global__ __launch_bounds__(256) void cand_score_kernel(int rows, int r, int V,
   double acc[kCandGroup];
 #pragma unroll
   for (int k = 0; k < kCandGroup; ++k) acc[k] = 0.0;
-  if (v < V) {
-    const __bf16* bp = Bm + (size_t)v * r + part * rq;
+  {
+    // the token's pieces are loaded kScoreBatch at a time (a token past V reads the
+    // last row and is not stored) before any is used, then taken in increasing j
+    const __bf16* bp = Bm + (size_t)min(v, V - 1) * r + part * rq;
     const float* zp = sz + part * rq;
-    for (int j0 = 0; j0 < rq; j0 += 8) {
-      const bf16x8 bv = *(const bf16x8*)(bp + j0);
+    for (int jb = 0; jb < rq; jb += 8 * kScoreBatch) {
+      bf16x8 bv[kScoreBatch];
 #pragma unroll
-      for (int k = 0; k < kCandGroup; ++k) {
-        if (k < gr) {
+      for (int q = 0; q < kScoreBatch; ++q) bv[q] = *(const bf16x8*)(bp + min(jb + 8 * q, rq - 8));
 #pragma unroll
-          for (int e = 0; e < 8; ++e)                  // bf16 x float32: exact in float64
-            acc[k] = fma((double)(float)bv[e], (double)zp[k * r + j0 + e], acc[k]);
+      for (int q = 0; q < kScoreBatch; ++q) {
+        const int j0 = jb + 8 * q;
+        if (j0 < rq) {
+#pragma unroll
+          for (int k = 0; k < kCandGroup; ++k) {
+            if (k < gr) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)              // bf16 x float32: exact in float64
+                acc[k] = fma((double)(float)bv[q][e], (double)zp[k * r + j0 + e], acc[k]);
+            }
+          }
         }
       }
     }
