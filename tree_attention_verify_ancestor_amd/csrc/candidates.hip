@@ -14,7 +14,8 @@
 //
 // Four kernels per call:
 //   cand_z_kernel      one wave per (row, j): z[row][j], lanes split d, float64 sums
-//   cand_score_kernel  four lanes per token (each a quarter of r), rows in groups of 8
+//   cand_score_kernel  four lanes per token (each a quarter of r), two tokens per
+//                      thread, rows in groups of 8
 //                      with z in LDS: the low-rank scores, written into the logits rows
 //   cand_select_kernel one workgroup per row: a lower bound on the C-th best score from
 //                      the threads' maxima, the few scores above it gathered in LDS and
@@ -86,56 +87,73 @@ __global__ __launch_bounds__(256) void cand_z_kernel(int d, int r, const __bf16*
   if (lane == 0) z[(size_t)row * r + j] = (float)s;
 }
 
+// TPT tokens per thread (token u at v0 + u * 64): each z value is read from LDS and
+// converted to float64 once for TPT products.  Every token's sum keeps the order of
+// one token per thread: j increasing, then the four quarters combined.
+template <int TPT>
 __global__ __launch_bounds__(256) void cand_score_kernel(int rows, int r, int V,
                                                         const __bf16* __restrict__ Bm,
                                                         const float* __restrict__ z,
                                                         float* __restrict__ logits) {
+  constexpr int kTok = 256 / kCandSplit;
   __shared__ float sz[kCandGroup * kCandMaxR];
   const int g0 = blockIdx.y * kCandGroup;
   const int gr = min(kCandGroup, rows - g0);
   for (int t = threadIdx.x; t < gr * r; t += blockDim.x) sz[t] = z[(size_t)g0 * r + t];
   __syncthreads();
-  const int v = blockIdx.x * (256 / kCandSplit) + threadIdx.x / kCandSplit;
+  const int v0 = blockIdx.x * kTok * TPT + threadIdx.x / kCandSplit;
   const int part = threadIdx.x % kCandSplit;
-  const int rq = r / kCandSplit;                         // a multiple of 8
-  double acc[kCandGroup];
+  const int rq = r / kCandSplit;
+  double acc[TPT][kCandGroup];
 #pragma unroll
-  for (int k = 0; k < kCandGroup; ++k) acc[k] = 0.0;
-  {
-    // the token's pieces are loaded kScoreBatch at a time (a token past V reads the
-    // last row and is not stored) before any is used, then taken in increasing j
-    const __bf16* bp = Bm + (size_t)min(v, V - 1) * r + part * rq;
-    const float* zp = sz + part * rq;
-    for (int jb = 0; jb < rq; jb += 8 * kScoreBatch) {
-      bf16x8 bv[kScoreBatch];
+  for (int u = 0; u < TPT; ++u)
 #pragma unroll
-      for (int q = 0; q < kScoreBatch; ++q) bv[q] = *(const bf16x8*)(bp + min(jb + 8 * q, rq - 8));
+    for (int k = 0; k < kCandGroup; ++k) acc[u][k] = 0.0;
+  const float* zp = sz + part * rq;
+  for (int jb = 0; jb < rq; jb += 8 * kScoreBatch) {
+    bf16x8 bv[TPT][kScoreBatch];
 #pragma unroll
-      for (int q = 0; q < kScoreBatch; ++q) {
-        const int j0 = jb + 8 * q;
-        if (j0 < rq) {
+    for (int u = 0; u < TPT; ++u) {
+      const __bf16* bp = Bm + (size_t)min(v0 + u * kTok, V - 1) * r + part * rq;
 #pragma unroll
-          for (int k = 0; k < kCandGroup; ++k) {
-            if (k < gr) {
+      for (int q = 0; q < kScoreBatch; ++q) bv[u][q] = *(const bf16x8*)(bp + min(jb + 8 * q, rq - 8));
+    }
 #pragma unroll
-              for (int e = 0; e < 8; ++e)              // bf16 x float32: exact in float64
-                acc[k] = fma((double)(float)bv[q][e], (double)zp[k * r + j0 + e], acc[k]);
+    for (int q = 0; q < kScoreBatch; ++q) {
+      const int j0 = jb + 8 * q;
+      if (j0 < rq) {
+#pragma unroll
+        for (int k = 0; k < kCandGroup; ++k) {
+          if (k < gr) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const double zv = (double)zp[k * r + j0 + e];
+#pragma unroll
+              for (int u = 0; u < TPT; ++u)
+                acc[u][k] = fma((double)(float)bv[u][q][e], zv, acc[u][k]);
             }
           }
         }
       }
     }
   }
-  // the four quarters of each dot, summed in a fixed order by every lane of the group
 #pragma unroll
-  for (int k = 0; k < kCandGroup; ++k) {
-    acc[k] += __shfl_xor(acc[k], 1);
-    acc[k] += __shfl_xor(acc[k], 2);
-  }
-  if (v < V && part == 0) {
+  for (int u = 0; u < TPT; ++u)
 #pragma unroll
-    for (int k = 0; k < kCandGroup; ++k)
-      if (k < gr) logits[(size_t)(g0 + k) * V + v] = (float)acc[k];
+    for (int k = 0; k < kCandGroup; ++k) {
+      acc[u][k] += __shfl_xor(acc[u][k], 1);
+      acc[u][k] += __shfl_xor(acc[u][k], 2);
+    }
+  if (part == 0) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int v = v0 + u * kTok;
+      if (v < V) {
+#pragma unroll
+        for (int k = 0; k < kCandGroup; ++k)
+          if (k < gr) logits[(size_t)(g0 + k) * V + v] = (float)acc[u][k];
+      }
+    }
   }
 }
 
@@ -375,8 +393,8 @@ TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C,
   float* z = (float*)ws;
   hipLaunchKernelGGL(tv::cand_z_kernel, dim3((r + 3) / 4, rows), dim3(256), 0, stream, d, r,
                      (const __bf16*)h, (const __bf16*)A, z);
-  constexpr int kTokensPerWg = 256 / tv::kCandSplit;
-  hipLaunchKernelGGL(tv::cand_score_kernel,
+  constexpr int kTokensPerWg = 256 / tv::kCandSplit * 2;
+  hipLaunchKernelGGL(tv::cand_score_kernel<2>,
                      dim3((vocab + kTokensPerWg - 1) / kTokensPerWg,
                           (rows + tv::kCandGroup - 1) / tv::kCandGroup),
                      dim3(256), 0, stream, rows, r, vocab, (const __bf16*)Bm, (const float*)z, logits);
