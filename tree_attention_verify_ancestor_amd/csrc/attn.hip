@@ -283,6 +283,13 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
     chunk = t % a.n_chunks;
     b = t / a.n_chunks;
   }
+  // the item is uniform over the workgroup (the ranked pick comes through LDS): keep it,
+  // and everything derived from it, in scalar registers so that branches on it are
+  // plain jumps
+  b = __builtin_amdgcn_readfirstlane(b);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  rb = __builtin_amdgcn_readfirstlane(rb);
   const int unit = (b * a.Hkv + kvh) * a.n_rb + rb;
 
   const int tid = threadIdx.x;
@@ -666,7 +673,182 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int p = 1; p < NBUF + 1; ++p)
       if (p < nst && p < NBUF + extra) issue(p);
-    if (!wave_live) {
+    if constexpr (WQ == 8 && WK == 1 && QT == 1) {
+      // ---- eight waves of one row tile: software-pipelined over 32-key subtiles.
+      // While a wave's softmax of subtile s runs on the vector ALUs, the products of
+      // subtile s+1 (S^T = K Q^T) run on the matrix core; then O^T += V^T P^T of subtile
+      // s with the row sums beside it, and K of subtile s+2 is read from LDS while those
+      // products run.  Both waves of a SIMD issue the same mixed stream, so the matrix
+      // core is fed from two waves (one wave alone issues products at about 3/4 of the
+      // peak rate).
+      //
+      // Stage x is opened (its DMAs waited for, then one barrier) just before the first
+      // read of its K.  At that barrier every wave has finished its reads of stage x-2,
+      // whose buffer is then refilled with stage x+2 (stages 0..NBUF-1 were issued above).
+      auto nsub = [&](int st) {
+        const int kb0 = stage_kbase(st);
+        const int ke = (has_tree && st == 0) ? n : c1;
+        return (min(kb0 + KT, ke) - kb0 + 31) >> 5;
+      };
+      auto open_stage = [&](int x) __attribute__((always_inline)) {
+        const int ahead = min(max(NBUF - 1, x + 1), nst - 1) - x;   // stages issued after x
+        if (ahead <= 0) wait_vmcnt<0>();
+        else if (ahead == 1) wait_vmcnt<DMA>();
+        else if (ahead == 2) wait_vmcnt<2 * DMA>();
+        else wait_vmcnt<3 * DMA>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS reads are done
+        lds_barrier();
+        if (x >= 2 && x + NBUF - 2 < nst) issue(x + NBUF - 2);
+      };
+      if (!wave_live) {
+        for (int x = 0; x < nst; ++x) open_stage(x);
+      } else {
+        KOps kr;                                  // K operands of the next subtile
+        f32x16 sa, sb;                            // scores of the current / next subtile
+        auto read_k = [&](int st, int sub) __attribute__((always_inline)) {
+          kr = load_k(smem + k_tile(st), sub);
+        };
+        float msub = 0.f;                         // the row's fixed reference
+        // One subtile s, in two phases whose issue order is pinned by scheduling fences:
+        //  1. the products of subtile s+1 (S^T = K Q^T from kr), each with its share of
+        //     the weights of s (fma, exp2, bf16 conversion) and two of the V^T reads of s;
+        //  2. O^T += V^T P^T of s; with KREAD each product with one K read of subtile
+        //     s+2 (st2, sub2) into kr (else the caller reads it after the step, behind
+        //     the barrier that opens its stage).  The row sum adds the float32 weights in
+        //     phase 1.
+        // Where s+1 or s+2 does not exist, valid LDS data is read and the result dropped.
+        auto step = [&](auto masked_tag, auto kread_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub,
+                        int st2, int sub2) __attribute__((always_inline)) {
+          constexpr bool MASKED = decltype(masked_tag)::value;
+          constexpr bool KREAD = decltype(kread_tag)::value;
+          constexpr int EPG = 16 / DS;             // weights per product of the next subtile
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const char* kb = smem + k_tile(st);
+          const uint32_t va0 = lds_addr(kb + v_tile(st)) + sub * 32 * ROWB + voff0;
+          if constexpr (MASKED) {
+            const bool tree = has_tree && st == 0;
+            apply_mask(s_cur, stage_kbase(st) + sub * 32 + 4 * g, tree ? n : c1,
+                       tree ? qanc[0] : ~0ull);
+          }
+          VOps v;
+          f32x16 sn = f32x16{};
+          float e[16];
+          bf16x2 pk[8];
+          float psum = 0.f;
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < DS; ++i) {
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr.v[i], qop[0][i], sn, 0, 0, 0);
+#pragma unroll
+            for (int j = i * EPG; j < (i + 1) * EPG; ++j)
+              e[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[j], a.sl2, -msub));
+            if (i > 0) {
+#pragma unroll
+              for (int j = (i - 1) * EPG; j < i * EPG; j += 2) {
+                pk[j >> 1] = bf16x2{(__bf16)e[j], (__bf16)e[j + 1]};
+                psum += e[j] + e[j + 1];              // the row sum of the float32 weights
+              }
+            }
+            {
+              // V^T operand (ks, dt) = i: rows 0-7 and 8-15 of its 16-key step
+              const int ks = i / DT, dt = i % DT;
+              const uint32_t lo_a = (va0 ^ (dt << 6)) + ks * 16 * ROWB;
+              const uint32_t hi_a = ((va0 ^ (dt << 6)) ^ VHI) + 8 * ROWB + ks * 16 * ROWB;
+              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)lo_a);
+              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)hi_a);
+              const s16x4 both[2] = {lo, hi};
+              v.v[ks][dt] = *(const bf16x8*)both;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int j = (DS - 1) * EPG; j < 16; j += 2) {
+            pk[j >> 1] = bf16x2{(__bf16)e[j], (__bf16)e[j + 1]};
+            psum += e[j] + e[j + 1];
+          }
+          l_run[0] += psum;
+          bf16x8 pb[2];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pb[j >> 2][2 * (j & 3)] = pk[j][0];
+            pb[j >> 2][2 * (j & 3) + 1] = pk[j][1];
+          }
+          const uint32_t ka0 = lds_addr(smem + k_tile(st2)) + sub2 * 32 * ROWB + koff0;
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[ks][dt], pb[ks], o[0][dt], 0, 0, 0);
+              if constexpr (KREAD) {
+                const int kx = ks * DT + dt;
+                kr.v[kx] = *(lds_bf16x8*)(uintptr_t)(ka0 ^ (kx << 5));
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          s_nxt = sn;
+        };
+        constexpr ic<0> unmasked{};
+        constexpr ic<1> masked{};
+        constexpr ic<0> no_kread{};
+        constexpr ic<1> kread{};
+
+        // subtile 0: its scores set the reference (the root is visible to every row in
+        // the tree stage; every key of a prefix stage is)
+        open_stage(0);
+        read_k(0, 0);
+        sa = qk(ic<0>{}, kr);
+        if (has_tree || n_full == 0)
+          apply_mask(sa, stage_kbase(0) + 4 * g, has_tree ? n : c1, has_tree ? qanc[0] : ~0ull);
+        reference(ic<0>{}, sa);
+        msub = m_run[0] == -INFINITY ? 0.f : m_run[0];
+        int x = 0;
+        if (has_tree) {
+          // the tree stage: one or two masked subtiles (the first one masked already)
+          const bool more = nst > 1;
+          const bool two1 = more && nsub(1) >= 2;          // stage 1 holds a second subtile
+          if (nsub(0) == 2) {
+            read_k(0, 1);
+            step(unmasked, no_kread, sa, sb, 0, 0, 0, 0);
+            if (more) open_stage(1);
+            read_k(more ? 1 : 0, 0);
+            step(masked, kread, sb, sa, 0, 1, two1 ? 1 : 0, 1);
+          } else {
+            if (more) open_stage(1);
+            read_k(more ? 1 : 0, 0);
+            step(unmasked, kread, sa, sb, 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
+            sa = sb;
+          }
+          x = 1;
+        } else if (nsub(0) >= 2) {
+          read_k(0, 1);
+        }
+        // full prefix stages: two unmasked subtiles each, the barrier that opens the next
+        // stage between them; one code path (where there is no next stage the K reads
+        // repeat this stage's)
+        const int full_end = has_tree + n_full;
+        for (; x < full_end; ++x) {
+          const bool more = x + 1 < nst;
+          const bool two = more && nsub(x + 1) >= 2;
+          step(unmasked, no_kread, sa, sb, x, 0, x, 0);
+          if (more) open_stage(x + 1);
+          read_k(more ? x + 1 : x, 0);
+          step(unmasked, kread, sb, sa, x, 1, two ? x + 1 : x, 1);
+        }
+        // a partial last prefix stage (masked; opened by the loop or above)
+        if (x < nst) {
+          if (nsub(x) >= 2) {
+            step(masked, kread, sa, sb, x, 0, x, 0);
+            step(masked, kread, sb, sa, x, 1, x, 1);
+          } else {
+            step(masked, kread, sa, sb, x, 0, x, 0);
+          }
+        }
+        // weights past the fixed reference's range show in the row sum (all terms are
+        // non-negative; inf and NaN included): the exact path below takes over
+        over = !(l_run[0] <= 0x1p48f);
+      }
+    } else if (!wave_live) {
       for (int st = 0; st < nst; ++st) begin_stage(st);
     } else {
       // The tree stage and a partial last prefix stage take the masked path outside the
