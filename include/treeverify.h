@@ -64,7 +64,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_SEQ_SECOND_ROOT 2  /* parent[i] == -1 for some i >= 1 */
 #define TV_SEQ_BAD_N 3        /* n_nodes (or the kept count m) outside [1, n_max] */
 #define TV_SEQ_NONFINITE 4    /* a draft-logit row holds NaN or +-Inf */
-#define TV_SEQ_BAD_PREFIX 5   /* prefix_offsets[b+1] - prefix_offsets[b] outside [0, max_prefix_len] */
+#define TV_SEQ_BAD_PREFIX 5   /* prefix_offsets[b] < 0, or offsets[b+1] - offsets[b] outside [0, max_prefix_len] */
 #define TV_SEQ_BAD_STATE 6    /* expansion step called out of order for this workspace */
 
 int tv_abi_version(void);
@@ -218,7 +218,11 @@ tv_status tree_budget_thresholds(const float* cost_us, int n_max, float threshol
  *   k_tree, v_tree [B][n_max][Hkv][D]   K/V of the tree nodes from this pass
  *   k_prefix, v_prefix [total][Hkv][D]  cached prefix, sequences packed back to back:
  *                  sequence b owns rows prefix_offsets[b] .. prefix_offsets[b+1]-1
- *   prefix_offsets int64 [B+1]          L_b = offsets[b+1] - offsets[b] <= max_prefix_len
+ *   prefix_offsets int64 [B+1]          L_b = offsets[b+1] - offsets[b] <= max_prefix_len;
+ *                  offsets[b] >= 0 and offsets[b+1] <= the rows of k_prefix / v_prefix
+ *                  (the caller's contract: the library cannot see the buffer's size; a
+ *                  negative offset or length, or a length past max_prefix_len, fails
+ *                  that sequence with TV_SEQ_BAD_PREFIX and nothing is read for it)
  *   n_nodes int32 [B], anc uint64 [B][n_max] (from tree_build)
  *   out            [B][n_max][Hq][D]    rows of padding nodes and failed sequences are 0
  *   lse fp32       [B][n_max][Hq]       nullable; 0 where out is 0
@@ -232,6 +236,19 @@ tv_status tree_budget_thresholds(const float* cost_us, int n_max, float threshol
  */
 size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
                                        int max_prefix_len);
+/*
+ * tree_verify_attn_plan -- the launch plan tree_verify_attn takes for these sizes (host
+ * only, no device call), for tests and diagnostics.  plan[8] (host, out):
+ *   plan[0] waves per workgroup      plan[1] row groups (waves splitting the rows)
+ *   plan[2] key splits (waves splitting each stage's keys)
+ *   plan[3] 32-row tiles per wave    plan[4] rows (node x query head of one KV head)
+ *           per workgroup            plan[5] keys per chunk
+ *   plan[6] key chunks               plan[7] workgroups launched (after padding)
+ * Returns TV_ERR_SHAPE / TV_ERR_UNSUPPORTED for sizes tree_verify_attn rejects, and
+ * TV_ERR_DTYPE for TV_F32 (one workgroup per output row, no plan).
+ */
+tv_status tree_verify_attn_plan(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
+                                int max_prefix_len, int32_t* plan);
 tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max,
                            int max_prefix_len, float scale, const void* q, const void* k_tree,
                            const void* v_tree, const void* k_prefix, const void* v_prefix,

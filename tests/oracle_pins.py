@@ -869,6 +869,122 @@ def pin_candidates_all_exact():
                for i in range(2) for v in range(V))
 
 
+# ---------------------------------------------------------------- indeterminate flags
+
+def _f32_midpoints(values):
+    """float64 midpoints between float32 values and their next float32 up (exact:
+    25 significant bits fit a float64)."""
+    f = np.asarray(values, dtype=np.float32)
+    hi = np.nextafter(f, np.float32(np.inf))
+    return (f.astype(np.float64) + hi.astype(np.float64)) / 2.0
+
+
+_FLAG_PROBES = np.array([1.2345678, -3.75e-3, 1234.5, 0.69314718, -41.0], dtype=np.float32)
+
+
+def pin_expand_midpoint_flag():
+    """The expansion's float64 log-normaliser is flagged exactly when it lies within
+    1e-12 (relative) of a float32 rounding midpoint -- on it included: values on a
+    midpoint, 1e-13 off either side are flagged; 1e-11 off, or on a float32 value
+    (half an ulp, about 6e-8, away) are not.  Then through expand_rerank: a row of V equal
+    logits l has the log-normaliser l + log V exactly as the oracle sums it; the search
+    below picks (l, V) next to a midpoint (flagged) and far from every one (not)."""
+    helper = oracle.expand._near_fp32_midpoint
+    for m in _f32_midpoints(_FLAG_PROBES):
+        for x, want in ((m, True), (m * (1 + 1e-13), True), (m * (1 - 1e-13), True),
+                        (m * (1 + 1e-11), False), (m * (1 - 1e-11), False),
+                        (float(np.float32(m)), False)):
+            if bool(helper(np.float64(x))) != want:
+                return False
+    Vs = np.arange(8, 1 << 17, dtype=np.int64)
+    logs = np.log(Vs.astype(np.float64))
+    near = far = None
+    for l in np.float32(0.5) + np.arange(64, dtype=np.float32) * np.float32(1.0 / 64):
+        lse = np.float64(l) + logs
+        f = lse.astype(np.float32)
+        d = np.minimum(np.abs(lse - _f32_midpoints(f)),
+                       np.abs(lse - _f32_midpoints(np.nextafter(f, np.float32(-np.inf)))))
+        hit = np.nonzero(d <= 2e-13 * np.abs(lse))[0]
+        if near is None and len(hit):
+            near = (l, int(Vs[hit[0]]))
+        if far is None:
+            miss = np.nonzero(d >= 1e-9 * np.abs(lse))[0]
+            far = (l, int(Vs[miss[0]])) if len(miss) else None
+        if near is not None and far is not None:
+            break
+    if near is None or far is None:
+        return False
+    for (l, V), want in ((near, True), (far, False)):
+        level = np.full((1, 1, V), l, dtype=np.float32)
+        res = oracle.expand_rerank([level], 2, 3, np.array([0], np.int32))
+        if bool(res.indeterminate[0]) != want:
+            return False
+    return True
+
+
+def pin_candidates_midpoint_flag():
+    """The candidate head flags a float64 dot product within 1e-12 (relative) of a
+    float32 rounding midpoint and not exactly on it (a sum on a midpoint was carried
+    exactly and rounds to even on both sides): 1e-13 off either side flagged; on it,
+    1e-11 off, or on a float32 value not."""
+    helper = oracle.candidates._fp32_near_midpoint
+    xs, want = [], []
+    for m in _f32_midpoints(_FLAG_PROBES):
+        for x, w in ((m, False), (m * (1 + 1e-13), True), (m * (1 - 1e-13), True),
+                     (m * (1 + 1e-11), False), (m * (1 - 1e-11), False),
+                     (float(np.float32(m)), False)):
+            xs.append(x)
+            want.append(w)
+    return bool(np.array_equal(helper(np.array(xs, dtype=np.float64)), np.array(want)))
+
+
+def _stoch_two_node(r_root, q_root, x, ua, ub):
+    """A root with one child of token x: target weights r (root row) and draft q;
+    the child's own target row is one-hot."""
+    V = len(r_root)
+    parent = np.array([[-1, 0]], np.int32)
+    tok = np.array([[0, x]], np.int32)
+    p = np.zeros((1, 2, V), np.float32)
+    p[0, 0] = r_root
+    p[0, 1, 0] = 1.0
+    q = np.zeros((1, 2, V), np.float32)
+    q[0, 0] = q_root
+    q[0, 1, 0] = 1.0
+    return oracle.tree_accept_stochastic(parent, tok, np.array([2], np.int32), p, q,
+                                         np.array([[0.0, ua]], np.float32),
+                                         np.array([ub], np.float32))
+
+
+def pin_stochastic_margins():
+    """Stochastic acceptance reports a sequence as indeterminate exactly when a decision
+    lies within 1e-9 (relative) of its threshold.  Target weights r = (1/2, 1/4, 1/4, t)
+    have the float64 sum S = 1 + t exactly.  The child of token 1 with draft q(1) = 1/2
+    and u = 1/2 is tested by u S q(1) = (1 + t) / 4 < r(1) = 1/4: it fails, with
+    relative margin t.  t = 2^-33 (1.2e-10) is flagged, t = 2^-28 (3.7e-9) is not, and
+    u one float32 step below 1/2 passes by 6e-8, unflagged.  The bonus draw of a root
+    without children is the first index whose running sum (1/2, 3/4, 1, 1 + t) passes
+    u S: u = 3/4 gives index 2 at 3/4 t (6.5e-11 for t = 2^-33) from the boundary
+    3/4, flagged; u = 0.6 gives index 1 far from both boundaries."""
+    q = np.array([0.25, 0.5, 0.25, 0.0], np.float32)
+    half_down = float(np.nextafter(np.float32(0.5), np.float32(0.0)))
+    for t, ua, want_pass, want_flag in ((2.0 ** -33, 0.5, False, True), (2.0 ** -28, 0.5, False, False),
+                                        (2.0 ** -33, half_down, True, False)):
+        r = np.array([0.5, 0.25, 0.25, t], np.float32)
+        alen, best, bonus, path, indet = _stoch_two_node(r, q, 1, ua, 0.6)
+        if bool(alen[0] == 1) != want_pass or bool(indet[0]) != want_flag:
+            return False
+    for t, ub, want_idx, want_flag in ((2.0 ** -33, 0.75, 2, True), (2.0 ** -33, 0.6, 1, False),
+                                       (2.0 ** -20, 0.75, 2, False)):
+        r = np.array([0.5, 0.25, 0.25, t], np.float32)
+        p = r[None, None, :].copy()
+        res = oracle.tree_accept_stochastic(np.array([[-1]], np.int32), np.zeros((1, 1), np.int32),
+                                            np.array([1], np.int32), p, p.copy(),
+                                            np.zeros((1, 1), np.float32), np.array([ub], np.float32))
+        if int(res[2][0]) != want_idx or bool(res[4][0]) != want_flag:
+            return False
+    return True
+
+
 ALL_PINS = {
     "tree_example": pin_tree_example,
     "tree_closed_forms": pin_tree_closed_forms,
@@ -903,6 +1019,9 @@ ALL_PINS = {
     "candidates_exact_dots": pin_candidates_exact_dots,
     "candidates_low_rank_exact": pin_candidates_low_rank_exact,
     "candidates_all_exact": pin_candidates_all_exact,
+    "expand_midpoint_flag": pin_expand_midpoint_flag,
+    "candidates_midpoint_flag": pin_candidates_midpoint_flag,
+    "stochastic_margins": pin_stochastic_margins,
 }
 
 

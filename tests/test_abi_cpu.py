@@ -167,6 +167,28 @@ def test_attn_workspace_size(L):
     assert L.tree_verify_attn_workspace_size(1, 1, 64, 32, 32, 128, 64) == 0
 
 
+def test_attn_plan(L):
+    """The launch-plan query: host only; each row-count regime takes its shape (a 70B-shaped
+    batch with 512 rows per KV head: eight waves of one 32-row tile, 256 rows a
+    workgroup, eight chunks of 4096 keys)."""
+    plan = (ctypes.c_int32 * 8)()
+    assert L.tree_verify_attn_plan(1, 4, 64, 64, 8, 128, 32768, plan) == OK
+    assert list(plan) == [8, 8, 1, 1, 256, 4096, 8, 512]
+    assert L.tree_verify_attn_plan(1, 2, 32, 2, 2, 128, 3000, plan) == OK
+    assert list(plan)[:5] == [4, 1, 4, 1, 32]
+    assert L.tree_verify_attn_plan(1, 2, 64, 4, 2, 128, 3000, plan) == OK
+    assert list(plan)[:5] == [8, 4, 2, 1, 128]
+    assert L.tree_verify_attn_plan(1, 1, 64, 32, 8, 128, 4096, plan) == OK   # few 256-row units
+    assert list(plan)[:5] == [4, 1, 4, 2, 64]
+    assert L.tree_verify_attn_plan(1, 1, 64, 32, 8, 128, 0, plan) == OK      # no prefix: one chunk
+    assert plan[6] == 1
+    assert L.tree_verify_attn_plan(0, 1, 64, 32, 8, 64, 100, plan) == DTYPE
+    assert L.tree_verify_attn_plan(1, 1, 64, 32, 8, 96, 100, plan) == UNSUP
+    assert L.tree_verify_attn_plan(1, 1, 65, 32, 8, 128, 100, plan) == SHAPE
+    assert L.tree_verify_attn_plan(1, 1, 64, 32, 5, 128, 100, plan) == SHAPE
+    assert L.tree_verify_attn_plan(1, 1, 64, 32, 8, 128, 100, None) == NULL
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libtreeverify.so")

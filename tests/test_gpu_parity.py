@@ -13,8 +13,8 @@ import oracle
 import oracle.attention
 import synth
 import tree_attention_verify_ancestor_amd as tv
-from gpu_helpers import (DEV, anc_u64, attn_close, attn_device_inputs, dev_i32, dev_input,
-                         host, run_attn, run_expand)
+from gpu_helpers import (DEV, anc_u64, attn_close, attn_device_inputs, dev_i32, dev_i64,
+                         dev_input, host, run_attn, run_expand)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,9 @@ def _check_expand(levels, k, m, roots, m_per_seq=None, budget_log=None):
     assert np.array_equal(st, ref.status)
     n = out.n_nodes.cpu().numpy()
     assert np.array_equal(n, ref.n_nodes)
+    # sequences whose log-normaliser lies next to a float32 midpoint are compared on
+    # status and size only; none does on these seeds
+    assert not ref.indeterminate.any(), f"{int(ref.indeterminate.sum())} sequences excluded"
     ok = ~ref.indeterminate
     assert np.array_equal(out.parent.cpu().numpy()[ok], ref.parent[ok])
     assert np.array_equal(out.token.cpu().numpy()[ok], ref.token[ok])
@@ -240,29 +243,157 @@ def test_attn_tiny_workload():
     _check_attn(synth.attention_inputs(w), parent, nn, "workload 1")
 
 
-@pytest.mark.parametrize("G,L", [(1, 100), (4, 0), (8, 3000)])
-def test_attn_one_hot_mask_exact(G, L):
-    """Tree V rows are unit vectors e_j and prefix V is 0 in the first 64 coordinates,
-    so out[i][h][j] must be exactly 0 for j off i's root path and > 0 on it."""
-    Hkv = 2
-    inp, parent, nn = synth.random_attention_case(31 + G, 2, G * Hkv, Hkv, 128, (L, L // 2 + 1),
-                                                  (64, 45), dtype="bf16", std=0.5)
+# Every launch shape of tree_verify_attn (name: batch, n_max, query heads per KV head, KV
+# heads, and the plan's waves / row groups / key splits / 32-row tiles per wave).
+ATTN_SHAPES = {
+    "32 rows: four waves split the keys": (2, 32, 1, 2, (4, 1, 4, 1)),
+    "64 rows: four waves, two tiles each": (2, 64, 1, 2, (4, 1, 4, 2)),
+    "256 rows in few units: 64-row units": (2, 64, 4, 2, (4, 1, 4, 2)),
+    "128 rows: four row groups x two key halves": (2, 64, 2, 2, (8, 4, 2, 1)),
+    "512 rows: eight waves of one tile": (4, 64, 8, 8, (8, 8, 1, 1)),
+}
+# the same shapes with nine ragged sequences (ranked by work where eight waves own one
+# tile each: the ranking applies from eight sequences on)
+RAGGED_SHAPES = {
+    "32 rows": (32, 1, 2, (4, 1, 4, 1)),
+    "64 rows": (64, 1, 2, (4, 1, 4, 2)),
+    "256 rows in few units": (64, 4, 1, (4, 1, 4, 2)),
+    "128 rows": (64, 2, 2, (8, 4, 2, 1)),
+    "512 rows": (64, 8, 8, (8, 8, 1, 1)),
+}
+RAGGED_LENS = (3000, 17, 0, 900, 2500, 64, 1200, 5, 640)
+
+
+def _plan_of(B, n_max, G, Hkv, D, lens):
+    p = tv.attn_plan(B, n_max, G * Hkv, Hkv, D, int(max(lens)))
+    return p, (p["waves"], p["row_groups"], p["key_splits"], p["tiles_per_wave"])
+
+
+def _one_hot_inputs(seed, B, n_max, G, Hkv, D, lens, ns):
+    """Tree V rows are unit vectors: node j's V is e_j; prefix V is 0 in coordinates
+    0..63.  Then out[i][h][j] (j < 64) is i's softmax weight of node j: exactly 0 off
+    i's root path and > 0 on it, whatever the tolerance."""
+    inp, parent, nn = synth.random_attention_case(seed, B, G * Hkv, Hkv, D, lens, ns, dtype="bf16",
+                                                  std=0.5, n_max=n_max)
     one = synth.bf16_bits(np.float32([1.0]))[0]
-    inp.v_tree[:] = 0
-    for j in range(64):
+    inp.v_tree[:, :, :, :64] = 0
+    for j in range(n_max):
         inp.v_tree[:, j, :, j] = one
     inp.v_prefix[:, :, :64] = 0
+    return inp, parent, nn
+
+
+def _assert_one_hot(o, parent, nn, n_max):
     anc, _, _, _ = oracle.tree_build(parent, nn, None)
-    out, _, _, _ = run_attn(attn_device_inputs(inp), parent, nn, int(np.diff(inp.prefix_offsets).max()))
-    o = host(out)
-    for b in range(2):
+    for b in range(len(nn)):
         for i in range(int(nn[b])):
-            on = np.array([(int(anc[b, i]) >> j) & 1 for j in range(64)], dtype=bool)
-            on[int(nn[b]):] = False
-            blk = o[b, i, :, :64]
-            assert np.all(blk[:, ~on] == 0.0), (b, i)
-            assert np.all(blk[:, on] > 0.0), (b, i)
-    assert np.all(o[1, int(nn[1]):] == 0.0)
+            on = np.array([(int(anc[b, i]) >> j) & 1 for j in range(n_max)], dtype=bool)
+            blk = o[b, i, :, :n_max]
+            assert np.all(blk[:, ~on] == 0.0), ("leak", b, i, np.nonzero(blk[:, ~on])[1][:5])
+            assert np.all(blk[:, on] > 0.0), ("lost", b, i)
+            assert np.all(o[b, i, :, n_max:64] == 0.0), (b, i)
+        assert np.all(o[b, int(nn[b]):] == 0.0), ("padding", b)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("shape", list(ATTN_SHAPES))
+def test_attn_one_hot_mask_exact(shape, D):
+    """The exact mask probe on every launch shape, with prefixes of several key chunks."""
+    B, n_max, G, Hkv, want = ATTN_SHAPES[shape]
+    lens = (3000, 1777) if B == 2 else (3000, 2100, 777, 0)
+    ns = (n_max, n_max - 5) if B == 2 else (n_max, 40, 1, n_max - 3)
+    plan, got = _plan_of(B, n_max, G, Hkv, D, lens)
+    assert got == want and plan["n_chunks"] > 1, plan
+    inp, parent, nn = _one_hot_inputs(31 + G + D + n_max, B, n_max, G, Hkv, D, lens, ns)
+    out, _, st, _ = run_attn(attn_device_inputs(inp), parent, nn, max(lens))
+    assert np.all(st.cpu().numpy() == 0)
+    _assert_one_hot(host(out), parent, nn, n_max)
+
+
+@pytest.mark.parametrize("shape", list(RAGGED_SHAPES))
+def test_attn_ragged_marker_exact(shape):
+    """Nine ragged sequences (prefix 0..3000): sequence b's prefix V carries 1 in
+    coordinate 64 + b and every other prefix and tree V is 0 in coordinates 64..127, so
+    out[b'][i][h][64 + b] must be exactly 0 for every b' != b (no sequence sees another's
+    prefix) and > 0 for b' == b with a prefix.  The tree one-hot probe runs beside it in
+    coordinates 0..63."""
+    n_max, G, Hkv, want = RAGGED_SHAPES[shape]
+    B, D = 9, 128
+    base = (64, 3, 20, 64, 1, 33, 50, 64, 10)
+    ns = tuple(min(n, n_max) for n in base)
+    plan, got = _plan_of(B, n_max, G, Hkv, D, RAGGED_LENS)
+    assert got == want, plan
+    inp, parent, nn = _one_hot_inputs(500 + n_max + G, B, n_max, G, Hkv, D, RAGGED_LENS, ns)
+    one = synth.bf16_bits(np.float32([1.0]))[0]
+    inp.v_tree[:, :, :, 64:] = 0
+    inp.v_prefix[:, :, 64:] = 0
+    offs = inp.prefix_offsets
+    for b in range(B):
+        inp.v_prefix[offs[b]:offs[b + 1], :, 64 + b] = one
+    out, _, st, _ = run_attn(attn_device_inputs(inp), parent, nn, max(RAGGED_LENS))
+    assert np.all(st.cpu().numpy() == 0)
+    o = host(out)
+    _assert_one_hot(o, parent, nn, n_max)
+    for bp in range(B):
+        rows = o[bp, :int(nn[bp])]
+        for b in range(B):
+            col = rows[:, :, 64 + b]
+            if b != bp:
+                assert np.all(col == 0.0), ("marker of", b, "seen by", bp)
+            elif RAGGED_LENS[b] > 0:
+                assert np.all(col > 0.0), ("own marker lost", b)
+            else:
+                assert np.all(col == 0.0), b
+        assert np.all(rows[:, :, 64 + B:] == 0.0), bp
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_attn_negative_prefix_offset(ragged):
+    """A sequence whose prefix offset is negative fails with TV_SEQ_BAD_PREFIX and its
+    rows are zero; nothing before the prefix buffer is read, and the other sequences are
+    exact (a ragged batch of nine takes the ranked order, whose work weights read the
+    offsets too)."""
+    B = 9 if ragged else 3
+    lens = RAGGED_LENS if ragged else (900, 1500, 64)
+    ns = (64, 3, 20, 64, 1, 33, 50, 64, 10) if ragged else (64, 30, 64)
+    inp, parent, nn = synth.random_attention_case(71 + B, B, 64, 8, 128, lens, ns, std=0.5)
+    bad = 1
+    offs = inp.prefix_offsets.copy()
+    offs[bad] = -64                          # a valid length past the front of the buffer
+    good = [b for b in range(B) if b != bad and offs[b + 1] - offs[b] == lens[b]]
+    d = attn_device_inputs(inp)
+    d["offsets"] = dev_i64(offs)
+    out, lse, st, _ = run_attn(d, parent, nn, int(max(offs[b + 1] - offs[b] for b in range(B))))
+    st = st.cpu().numpy()
+    assert st[bad] == 5                                           # TV_SEQ_BAD_PREFIX
+    o = host(out)
+    assert np.all(o[bad] == 0.0) and np.all(lse.cpu().numpy()[bad] == 0.0)
+    ref, _ = oracle.tree_verify_attn(inp.f32("q"), inp.f32("k_tree"), inp.f32("v_tree"),
+                                     inp.f32("k_prefix"), inp.f32("v_prefix"), offs, parent, nn,
+                                     batches=good)
+    for b in good:
+        assert st[b] == 0
+        ok, msg = attn_close(o[b], ref[b], f"sequence {b}")
+        assert ok, msg
+
+
+def test_attn_negative_prefix_offset_fp32():
+    inp, parent, nn = synth.random_attention_case(73, 3, 4, 2, 64, (40, 100, 7), (10, 64, 5),
+                                                  dtype="f32", std=0.5)
+    offs = inp.prefix_offsets.copy()
+    offs[0] = -8
+    d = attn_device_inputs(inp)
+    d["offsets"] = dev_i64(offs)
+    out, lse, st, _ = run_attn(d, parent, nn, 100)
+    st = st.cpu().numpy()
+    assert st[0] == 5 and st[1] == 0 and st[2] == 0
+    o = host(out)
+    assert np.all(o[0] == 0.0)
+    ref, _ = oracle.tree_verify_attn(inp.q, inp.k_tree, inp.v_tree, inp.k_prefix, inp.v_prefix,
+                                     offs, parent, nn, batches=[1, 2])
+    for b in (1, 2):
+        ok, msg = attn_close(o[b], ref[b], f"fp32 sequence {b}")
+        assert ok, msg
 
 
 @pytest.mark.parametrize("G,n_max", [(8, 64), (4, 30), (1, 64), (1, 20)])
@@ -327,42 +458,16 @@ def test_attn_workload3_full():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("wid", [4, 5])
-def test_attn_workload_sampled(wid):
-    """Full-size workloads 4 and 5 in the bench's launch configuration; the oracle
-    recomputes a seeded sample of output rows one by one."""
+def test_attn_workload_full(wid):
+    """Full-size workloads 4 and 5 in the bench's launch configuration (trees from the
+    workload's expansion, max prefix = the longest sequence), every output element and
+    lse against the float64 oracle."""
     w = synth.WORKLOADS[wid]
     kc = synth.kept_counts(w) if isinstance(w.m, tuple) else None
     tree = oracle.expand_rerank(synth.draft_logits(w), w.k, w.m if kc is None else kc,
                                 synth.root_tokens(w))
     inp = synth.attention_inputs(w)
-    lens = np.diff(inp.prefix_offsets)
-    out, lse, st, _ = run_attn(attn_device_inputs(inp), tree.parent, tree.n_nodes, int(lens.max()))
-    assert np.all(st.cpu().numpy() == 0)
-    o = host(out)
-    l = lse.cpu().numpy()
-    rng = np.random.default_rng(wid)
-    picks = {}
-    for _ in range(48):
-        b = int(rng.integers(0, w.B))
-        picks.setdefault(b, []).append((int(rng.integers(0, w.Hq)), int(rng.integers(0, tree.n_nodes[b]))))
-    for b, hi in picks.items():
-        o0, o1 = int(inp.prefix_offsets[b]), int(inp.prefix_offsets[b + 1])
-        one = dict(q=synth.bf16_to_f32(inp.q[b:b + 1]),
-                   k_tree=synth.bf16_to_f32(inp.k_tree[b:b + 1]),
-                   v_tree=synth.bf16_to_f32(inp.v_tree[b:b + 1]),
-                   k_prefix=synth.bf16_to_f32(inp.k_prefix[o0:o1]),
-                   v_prefix=synth.bf16_to_f32(inp.v_prefix[o0:o1]))
-        offs = np.array([0, o1 - o0], dtype=np.int64)
-        for h, i in hi:
-            ref, ref_l = oracle.attention.tree_verify_attn_one(
-                one["q"], one["k_tree"], one["v_tree"], one["k_prefix"], one["v_prefix"], offs,
-                tree.parent[b:b + 1], 0, h, i)
-            ok, msg = attn_close(o[b, i, h], ref, f"workload {wid} b={b} h={h} i={i}")
-            assert ok, msg
-            assert abs(float(l[b, i, h]) - ref_l) <= 2e-2
-    # padding rows are zero
-    for b in range(w.B):
-        assert np.all(o[b, int(tree.n_nodes[b]):] == 0.0)
+    _check_attn(inp, tree.parent, tree.n_nodes, f"workload {wid}")
 
 
 # ----------------------------------------------------------------------------- whole path
@@ -507,8 +612,8 @@ def test_accept_stochastic_matches_oracle(seed, B, V):
     parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V)
     alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
     alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    assert not indet.any(), f"{int(indet.sum())} sequences excluded"     # none on these seeds
     ok = ~indet
-    assert ok.sum() >= B - 1
     assert np.array_equal(alen[ok], alen_r[ok])
     assert np.array_equal(best[ok], best_r[ok])
     assert np.array_equal(bonus[ok], bonus_r[ok])
@@ -698,13 +803,15 @@ def test_candidate_logits_matches_oracle(seed, rows, d, r, V, C):
     lg, cd = tv.tree_candidate_logits(_bf16_dev(hb), _bf16_dev(Ab), _bf16_dev(Bb), _bf16_dev(Wb), C)
     torch.cuda.synchronize()
     lg, cd = lg.cpu().numpy(), cd.cpu().numpy()
+    # entries next to a float32 midpoint (the oracle's float64 sum could round either
+    # way in another order) are excluded: 0-9 of them per case on these seeds, never a
+    # candidate list
+    assert int(rind.sum()) <= 16, f"{int(rind.sum())} entries excluded"
+    assert not rcind.any(), f"{int(rcind.sum())} candidate lists excluded"
     ok = ~rind
-    assert ok.mean() > 0.99
     assert np.array_equal(lg.view(np.uint32)[ok], ref.view(np.uint32)[ok])
     for i in range(rows):
-        if not rcind[i]:
-            assert np.array_equal(cd[i], rc[i]), i
-    assert not rcind.all()
+        assert np.array_equal(cd[i], rc[i]), i
 
 
 @pytest.mark.parametrize("V", [3000, 40000])
@@ -720,11 +827,10 @@ def test_candidate_logits_tied_scores(V):
         lg, cd = tv.tree_candidate_logits(_bf16_dev(hb), _bf16_dev(Ab), _bf16_dev(Bb), _bf16_dev(Wb), C)
         torch.cuda.synchronize()
         lg, cd = lg.cpu().numpy(), cd.cpu().numpy()
-        ok = ~rind
-        assert np.array_equal(lg.view(np.uint32)[ok], ref.view(np.uint32)[ok])
+        assert not rind.any() and not rcind.any()          # nothing excluded on this seed
+        assert np.array_equal(lg.view(np.uint32), ref.view(np.uint32))
         for i in range(4):
-            if not rcind[i]:
-                assert np.array_equal(cd[i], rc[i]), (C, i)
+            assert np.array_equal(cd[i], rc[i]), (C, i)
 
 
 def test_candidate_head_feeds_expansion():

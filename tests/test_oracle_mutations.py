@@ -65,6 +65,14 @@ def _attend_lse_without_max(qrows, keys, values, mask_rows, scale):
 
 _ORIG_ATTEND = oracle.attention._attend
 
+
+def _midpoint_dist(x64):
+    """Distance of float64 x to the nearest float32 rounding midpoint."""
+    f = np.float32(x64)
+    lo = np.float64(np.nextafter(f, np.float32(-np.inf)))
+    hi = np.float64(np.nextafter(f, np.float32(np.inf)))
+    return min(abs(x64 - (np.float64(f) + lo) / 2), abs(x64 - (np.float64(f) + hi) / 2))
+
 MUTATIONS = {
     "tree: walk drops the node itself": [(oracle.tree, "path_to_root", _walk_without_self)],
     "tree: walk index off by one": [(oracle.tree, "path_to_root", _walk_off_by_one)],
@@ -114,6 +122,23 @@ MUTATIONS = {
     "candidates: lowest scores selected": [
         (oracle.candidates, "top_candidates",
          lambda s, C: np.argsort(np.asarray(s, np.float32), kind="stable")[:C])],
+    "expand: midpoint window too wide": [
+        (oracle.expand, "_near_fp32_midpoint", lambda x: _midpoint_dist(x) <= 1e-10 * abs(x))],
+    "expand: midpoint window too narrow": [
+        (oracle.expand, "_near_fp32_midpoint", lambda x: _midpoint_dist(x) <= 1e-14 * abs(x))],
+    "expand: distance taken to the float32 value": [
+        (oracle.expand, "_near_fp32_midpoint", lambda x: abs(x - float(np.float32(x))) <= 1e-12 * abs(x))],
+    "candidates: midpoint window too wide": [
+        (oracle.candidates, "_fp32_near_midpoint",
+         lambda x: np.vectorize(lambda v: 0 < _midpoint_dist(v) <= 1e-10 * abs(v))(np.asarray(x, np.float64)))],
+    "candidates: midpoint window too narrow": [
+        (oracle.candidates, "_fp32_near_midpoint",
+         lambda x: np.vectorize(lambda v: 0 < _midpoint_dist(v) <= 1e-14 * abs(v))(np.asarray(x, np.float64)))],
+    "candidates: a sum on the midpoint flagged": [
+        (oracle.candidates, "_fp32_near_midpoint",
+         lambda x: np.vectorize(lambda v: _midpoint_dist(v) <= 1e-12 * abs(v))(np.asarray(x, np.float64)))],
+    "stochastic: decision window too wide": [(oracle.stochastic, "_EPS", 1e-6)],
+    "stochastic: decision window too narrow": [(oracle.stochastic, "_EPS", 1e-12)],
     "compact: one node short": [
         (oracle.compact, "kept_nodes", lambda row, n: [] if n < 0 else [0] + [int(row[j]) for j in range(n - 1)])],
 }

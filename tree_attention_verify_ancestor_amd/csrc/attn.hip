@@ -239,11 +239,11 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
     if (threadIdx.x == 0) *s_ragged = 0;
     __syncthreads();
     const int n0 = a.n_nodes[0];
-    const int64_t L0 = a.offsets[1] - a.offsets[0];
+    const int64_t L0 = a.offsets[0] < 0 ? -1 : a.offsets[1] - a.offsets[0];
     for (int j = threadIdx.x; j < P; j += blockDim.x) {
       const int bj = j / a.n_chunks, cj = j % a.n_chunks;
       const int nj = a.n_nodes[bj];
-      const int64_t Lj = a.offsets[bj + 1] - a.offsets[bj];
+      const int64_t Lj = a.offsets[bj] < 0 ? -1 : a.offsets[bj + 1] - a.offsets[bj];
       if (nj != n0 || Lj != L0) *s_ragged = 1;
       int w = 0;
       if (nj >= 1 && nj <= a.n_max && Lj >= 0 && Lj <= a.max_prefix) {
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   const int64_t off = a.offsets[b];
   const int64_t Lw = a.offsets[b + 1] - off;
   const bool n_ok = n >= 1 && n <= a.n_max;
-  const bool seq_ok = n_ok && Lw >= 0 && Lw <= a.max_prefix;
+  const bool seq_ok = n_ok && off >= 0 && Lw >= 0 && Lw <= a.max_prefix;
   const int L = seq_ok ? (int)Lw : 0;
   const int G = a.G;
   const int R = n_ok ? n * G : 0;
@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(kCombineLanes * CR) void attn_combine(AttnArgs a) {
   const int b = row / (a.Hq * a.n_max);
   const int n = a.n_nodes[b];
   const int64_t Lw = a.offsets[b + 1] - a.offsets[b];
-  if (n < 1 || n > a.n_max || Lw < 0 || Lw > a.max_prefix || i >= n) return;
+  if (n < 1 || n > a.n_max || a.offsets[b] < 0 || Lw < 0 || Lw > a.max_prefix || i >= n) return;
   const int L = (int)Lw;
   const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
   if (nc <= 1) return;
@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(128) void attn_f32(
   const int64_t Lw = offsets[b + 1] - off;
   int status = TV_SEQ_OK;
   if (n < 1 || n > n_max) status = TV_SEQ_BAD_N;
-  else if (Lw < 0 || Lw > max_prefix) status = TV_SEQ_BAD_PREFIX;
+  else if (off < 0 || Lw < 0 || Lw > max_prefix) status = TV_SEQ_BAD_PREFIX;
   if (seq_status && i == 0 && h == 0 && tid == 0) seq_status[b] = status;
   const size_t orow = (((size_t)b * n_max + i) * Hq + h);
   if (status != TV_SEQ_OK || i >= n) {
@@ -1218,6 +1218,21 @@ TV_API size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int
       max_prefix_len < 0 || (D != 64 && D != 128))
     return 0;
   return tv::make_plan(B, n_max, Hq, Hkv, D, max_prefix_len).ws_bytes;
+}
+
+TV_API tv_status tree_verify_attn_plan(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
+                                       int max_prefix_len, int32_t* plan) {
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_DTYPE;
+  if (!plan) return TV_ERR_NULL;
+  if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      max_prefix_len < 0 || D < 1)
+    return TV_ERR_SHAPE;
+  if (dt == TV_F32) return TV_ERR_DTYPE;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  const tv::AttnPlan p = tv::make_plan(B, n_max, Hq, Hkv, D, max_prefix_len);
+  const int32_t v[8] = {p.waves, p.wq, p.wk, p.qt, p.rows_per_wg, p.chunk_keys, p.n_chunks, p.grid};
+  for (int i = 0; i < 8; ++i) plan[i] = v[i];
+  return TV_OK;
 }
 
 TV_API tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max,

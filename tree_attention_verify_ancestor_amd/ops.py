@@ -165,6 +165,16 @@ def attn_workspace(dtype, B, n_max, Hq, Hkv, D, max_prefix_len, device="cuda"):
     return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
 
 
+def attn_plan(B, n_max, Hq, Hkv, D, max_prefix_len, dtype=torch.bfloat16):
+    """The launch plan of tree_verify_attn for these sizes, as a dict (host only)."""
+    plan = (ctypes.c_int32 * 8)()
+    check("tree_verify_attn_plan", lib().tree_verify_attn_plan(_DT[dtype], B, n_max, Hq, Hkv, D,
+                                                                max_prefix_len, plan))
+    keys = ("waves", "row_groups", "key_splits", "tiles_per_wave", "rows_per_wg", "chunk_keys",
+            "n_chunks", "grid")
+    return dict(zip(keys, list(plan)))
+
+
 def tree_verify_attn(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, n_nodes, anc,
                      max_prefix_len, scale=0.0, out=None, lse=None, ws=None, seq_status=None,
                      want_lse=True):
