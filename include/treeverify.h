@@ -257,6 +257,25 @@ tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max
                            int32_t* seq_status, hipStream_t stream);
 
 /*
+ * tree_verify_attn_noalloc -- tree_verify_attn for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same arguments, results and kernels as tree_verify_attn, without ws / ws_bytes: the
+ * chunk partials go to a fixed 128 MiB device array of the library (one per GPU, held
+ * until the process ends; it needs no initialisation).  Nothing is allocated or freed.
+ * Returns TV_ERR_WORKSPACE when the partials of these sizes exceed 128 MiB
+ * (tree_verify_attn_workspace_size(...) > 134217728), TV_ERR_HIP if the array's device
+ * address cannot be read.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (concurrent streams, or host threads) race and must be ordered by
+ * the caller.
+ */
+tv_status tree_verify_attn_noalloc(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max,
+                                   int max_prefix_len, float scale, const void* q,
+                                   const void* k_tree, const void* v_tree, const void* k_prefix,
+                                   const void* v_prefix, const int64_t* prefix_offsets,
+                                   const int32_t* n_nodes, const uint64_t* anc, void* out,
+                                   float* lse, int32_t* seq_status, hipStream_t stream);
+
+/*
  * tree_accept -- greedy acceptance of the longest matching path.
  * [EAGLE] "Well-Calibrated Draft Model": under greedy decoding a draft token is
  * accepted when it is the target's most likely token.  [EAGLE-3] section 4 step 4:

@@ -13,6 +13,7 @@ TV_F32, TV_BF16 = 0, 1
 EXPORTS = ("tv_abi_version", "tv_status_string", "tree_build", "tree_expand_workspace_size",
            "tree_expand_rerank", "tree_draft_continue", "tree_budget_thresholds",
            "tree_verify_attn_workspace_size", "tree_verify_attn_plan", "tree_verify_attn",
+           "tree_verify_attn_noalloc",
            "tree_accept", "tree_accept_stochastic", "tree_kv_compact",
            "tree_candidate_workspace_size", "tree_candidate_logits")
 
@@ -34,6 +35,8 @@ _SIGNATURES = {
     "tree_verify_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "tree_verify_attn": (_I, [_I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _P, _P, _S, _P, _P]),
+    "tree_verify_attn_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, _P, _P]),
     "tree_accept": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tree_accept_stochastic": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P]),

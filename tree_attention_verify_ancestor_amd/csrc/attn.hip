@@ -36,6 +36,8 @@
 // fp32 workloads are small correctness cases).
 #include <math.h>
 
+#include <mutex>
+
 #include <stdint.h>
 
 #include <type_traits>
@@ -1211,6 +1213,32 @@ static bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
 
 }  // namespace tv
 
+namespace tv {
+
+// Scratch of tree_verify_attn_noalloc: the fp32 chunk partials in a fixed device array
+// (one copy per GPU, held until the process ends) instead of a caller workspace.  Host
+// code reaches it only through the device address hipGetSymbolAddress returns for the
+// current device, kept per device; the array's name is not a device address on the host.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+static void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+}  // namespace tv
+
 TV_API size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int Hq, int Hkv,
                                               int D, int max_prefix_len) {
   if (dt != TV_BF16) return 0;
@@ -1296,4 +1324,23 @@ TV_API tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, in
   if (D == 128) tv::launch_bf16<128>(p, a, stream);
   else tv::launch_bf16<64>(p, a, stream);
   return tv::launch_status();
+}
+
+TV_API tv_status tree_verify_attn_noalloc(tv_dtype dt, int B, int Hq, int Hkv, int D, int n_max,
+                                          int max_prefix_len, float scale, const void* q,
+                                          const void* k_tree, const void* v_tree,
+                                          const void* k_prefix, const void* v_prefix,
+                                          const int64_t* prefix_offsets, const int32_t* n_nodes,
+                                          const uint64_t* anc, void* out, float* lse,
+                                          int32_t* seq_status, hipStream_t stream) {
+  const size_t need = tree_verify_attn_workspace_size(dt, B, n_max, Hq, Hkv, D, max_prefix_len);
+  if (need > tv::kScratchBytes) return TV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = tv::scratch_of_current_device();
+    if (!ws) return TV_ERR_HIP;
+  }
+  return tree_verify_attn(dt, B, Hq, Hkv, D, n_max, max_prefix_len, scale, q, k_tree, v_tree,
+                          k_prefix, v_prefix, prefix_offsets, n_nodes, anc, out, lse, ws,
+                          need > 0 ? tv::kScratchBytes : 0, seq_status, stream);
 }

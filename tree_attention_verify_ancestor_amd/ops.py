@@ -217,6 +217,40 @@ def tree_verify_attn(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, n_no
     return out, lse, seq_status
 
 
+def tree_verify_attn_noalloc(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, n_nodes, anc,
+                             max_prefix_len, out, seq_status, lse=None, scale=0.0):
+    """tree_verify_attn without a workspace: the library's fixed per-GPU scratch holds
+    the chunk partials.  The caller passes every output (out, seq_status, optional lse),
+    so this call allocates nothing."""
+    dt = q.dtype
+    if dt not in _DT:
+        raise TypeError(f"q must be float32 or bfloat16, got {q.dtype}")
+    _need(q, "q", dt, 4)
+    B, n_max, Hq, D = q.shape
+    _need(k_tree, "k_tree", dt, 4)
+    Hkv = k_tree.shape[2]
+    _need(k_tree, "k_tree", dt, shape=(B, n_max, Hkv, D))
+    _need(v_tree, "v_tree", dt, shape=(B, n_max, Hkv, D))
+    _need(k_prefix, "k_prefix", dt, 3)
+    _need(v_prefix, "v_prefix", dt, shape=tuple(k_prefix.shape))
+    if k_prefix.shape[1:] != (Hkv, D):
+        raise ValueError(f"k_prefix must be [total][{Hkv}][{D}], got {tuple(k_prefix.shape)}")
+    _need(prefix_offsets, "prefix_offsets", torch.int64, shape=(B + 1,))
+    _need(n_nodes, "n_nodes", torch.int32, shape=(B,))
+    _need(anc, "anc", torch.int64, shape=(B, n_max))
+    _need(out, "out", dt, shape=(B, n_max, Hq, D))
+    _need(seq_status, "seq_status", torch.int32, shape=(B,))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, n_max, Hq))
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    check("tree_verify_attn_noalloc", lib().tree_verify_attn_noalloc(
+        _DT[dt], B, Hq, Hkv, D, n_max, int(max_prefix_len), float(scale), _ptr(q), _ptr(k_tree),
+        _ptr(v_tree), _ptr(kp), _ptr(vp), _ptr(prefix_offsets), _ptr(n_nodes), _ptr(anc),
+        _ptr(out), _ptr(lse), _ptr(seq_status), _stream()))
+    return out, lse, seq_status
+
+
 def tree_accept(parent, depth, anc, n_nodes, token, target_next, want_path=True):
     """(accept_len, best_node, bonus_token, path) -- int32 tensors."""
     _need(parent, "parent", torch.int32, 2)
