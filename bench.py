@@ -303,10 +303,10 @@ def gpu_leg(args, inp):
     compact_bytes = rows_written / R * w.Hkv * w.D * el * 2 * 2      # K and V, read and write
 
     # stochastic (rejection-sampling) acceptance on the first copy's tree, with seeded
-    # target / draft distributions over the workload's vocabulary, when they fit
+    # target / draft distributions over the workload's vocabulary (up to 512 MiB of them)
     stoch = None
     V = int(w.V)
-    if V <= 36864 and w.B * w.n_max * V * 8 <= (256 << 20):
+    if w.B * w.n_max * V * 8 <= (512 << 20):
         rng = np.random.default_rng(77)
         lq = rng.standard_normal((w.B, w.n_max, V), dtype=np.float32) * 2
         lp = lq + rng.standard_normal((w.B, w.n_max, V), dtype=np.float32) * np.float32(0.7)

@@ -327,8 +327,9 @@ tv_status tree_accept(int B, int n_max, const int32_t* parent, const int32_t* de
  *   u_bonus    float32 [B]         uniform in [0,1) for the bonus token
  *   accept_len, best_node, bonus_token int32 [B], path int32 [B][n_max] (nullable):
  *                 as for tree_accept
- * 1 <= vocab <= 36864 (else TV_ERR_UNSUPPORTED; the weights live in LDS).  Tokens
- * outside [0, vocab) fail.
+ * vocab >= 1.  Up to 36864 tokens the weights r live in LDS; past that they are
+ * recomputed from p_target and q_draft on every pass over the vocabulary (same bits),
+ * so each rejection streams two rows instead of one.  Tokens outside [0, vocab) fail.
  * Sums in float64 depend on their order in the last bits: a decision within ~1e-15
  * (relative) of its threshold may differ from a sequential evaluation.
  */

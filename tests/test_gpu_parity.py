@@ -621,9 +621,53 @@ def test_accept_stochastic_matches_oracle(seed, B, V):
     assert alen_r.max() >= 1                                         # some candidates passed
 
 
-def test_accept_stochastic_greedy_limit_equals_tree_accept():
-    """One-hot target rows: the device's stochastic walk equals its greedy acceptance."""
-    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(9, 6, 300, one_hot=True)
+def test_accept_stochastic_workload4_vocab():
+    """The 70B-shaped workload's own dynamic trees (four sequences of 64 nodes) over its
+    128256-token vocabulary, past the LDS cap, against the oracle bit for bit."""
+    w = synth.WORKLOADS[4]
+    tree = oracle.expand_rerank(synth.draft_logits(w), w.k, w.m, synth.root_tokens(w))
+    B, n_max, V = w.B, w.n_max, w.V
+    rng = np.random.default_rng(404)
+    lq = rng.standard_normal((B, n_max, V), dtype=np.float32) * np.float32(2.0)
+    lp = lq + rng.standard_normal((B, n_max, V), dtype=np.float32) * np.float32(0.7)
+    sm = lambda x: (np.exp(x - x.max(-1, keepdims=True)) / np.exp(x - x.max(-1, keepdims=True)).sum(-1, keepdims=True))
+    q = sm(lq.astype(np.float64)).astype(np.float32)
+    p = sm(lp.astype(np.float64)).astype(np.float32)
+    tok = np.zeros((B, n_max), np.int32)
+    parent, nn = tree.parent, tree.n_nodes
+    for b in range(B):
+        for u in range(int(nn[b])):
+            kids = [c for c in range(1, int(nn[b])) if parent[b, c] == u]
+            if kids:
+                wts = q[b, u].astype(np.float64)
+                tok[b, kids] = rng.choice(V, size=len(kids), replace=False, p=wts / wts.sum())
+    ua = rng.random((B, n_max)).astype(np.float32)
+    ub = rng.random(B).astype(np.float32)
+    alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    assert not indet.any(), f"{int(indet.sum())} sequences excluded"
+    assert np.array_equal(alen, alen_r) and np.array_equal(best, best_r)
+    assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
+    assert alen_r.max() >= 1
+
+
+@pytest.mark.parametrize("seed,B,V", [(12, 5, 40000), (13, 3, 200003)])
+def test_accept_stochastic_large_vocab(seed, B, V):
+    """Vocabularies past the LDS cap (weights recomputed from p and q every pass),
+    against the oracle bit for bit."""
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V)
+    alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    assert not indet.any(), f"{int(indet.sum())} sequences excluded"
+    assert np.array_equal(alen, alen_r) and np.array_equal(best, best_r)
+    assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
+
+
+@pytest.mark.parametrize("V", [300, 50000])
+def test_accept_stochastic_greedy_limit_equals_tree_accept(V):
+    """One-hot target rows: the device's stochastic walk equals its greedy acceptance
+    (r in LDS, and recomputed past the LDS cap)."""
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(9, 6, V, one_hot=True)
     alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
     par_d, nn_d = dev_i32(parent), dev_i32(nn)
     anc, depth, _, _ = tv.tree_build(par_d, nn_d)

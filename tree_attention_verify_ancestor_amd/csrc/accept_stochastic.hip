@@ -16,10 +16,14 @@
 // When no child passes the bonus token is the first v whose running sum of r passes
 // u_bonus * S.
 //
-// One workgroup of 1024 threads per sequence walks the tree.  The current weights r
-// live in LDS (vocab <= 36864 floats); rows of p_target and q_draft stream from HBM
-// with coalesced loads.  Sums are float64: per thread (strided elements for the
-// totals, a contiguous slice for the bonus's running sum), then over the workgroup
+// One workgroup of 1024 threads per sequence walks the tree.  Up to 36864 tokens the
+// current weights r live in LDS; rows of p_target and q_draft stream from HBM with
+// coalesced loads.  Past that (a 128256-token vocabulary) r is never stored: after k
+// rejections at the current node, r[v] is the node's p_target[v] taken through the k
+// residual steps with the k scalars fl32(S_j) kept in LDS -- the same float32
+// operations in the same order, so the same bits -- and every pass streams the node's
+// p_target and q_draft rows.  Sums are float64: per thread (strided elements for the
+// totals; contiguous elements for the bonus's running sum), then over the workgroup
 // in a fixed order.
 #include "tv_internal.h"
 
@@ -196,6 +200,168 @@ __global__ __launch_bounds__(kStochThreads) void accept_stochastic_kernel(
   if (path && tid < n_max) path[row + tid] = tid < depth ? schain[tid] : -1;
 }
 
+// Vocabularies past the LDS: r replayed from the node's p_target row (see the header).
+constexpr int kStochScan = 4;                 // contiguous tokens per thread in the bonus scan
+
+__global__ __launch_bounds__(kStochThreads) void accept_stochastic_stream_kernel(
+    int n_max, int V, const int32_t* __restrict__ parent, const uint64_t* __restrict__ anc,
+    const int32_t* __restrict__ n_nodes, const int32_t* __restrict__ token,
+    const float* __restrict__ p_target, const float* __restrict__ q_draft,
+    const float* __restrict__ u_accept, const float* __restrict__ u_bonus,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ best_node,
+    int32_t* __restrict__ bonus_token, int32_t* __restrict__ path) {
+  __shared__ float sS32[TV_MAX_NODES];        // fl32(S) of each rejection at the current node
+  __shared__ double sred[kStochThreads / 64];
+  __shared__ double sscan[kStochThreads / 64];
+  __shared__ int skids[TV_MAX_NODES];
+  __shared__ int snkids;
+  __shared__ int schain[TV_MAX_NODES];
+  __shared__ int spick, slastpos;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t row = (size_t)b * n_max;
+  const int n = n_nodes[b];
+  const bool valid = n >= 1 && n <= n_max && anc[row] == 1ull;
+  if (!valid) {
+    if (tid == 0) {
+      accept_len[b] = -1;
+      best_node[b] = -1;
+      bonus_token[b] = -1;
+    }
+    if (path && tid < n_max) path[row + tid] = -1;
+    return;
+  }
+  int u = 0, depth = 0, nrej = 0;
+  const float* pr = p_target + row * V;                    // node u's rows
+  const float* q = q_draft + row * V;
+  // r[v] after the nrej residual steps at u: product then difference, each float32
+  auto r_of = [&](float pv, float qv) {
+    float r = pv;
+    for (int j = 0; j < nrej; ++j) {
+#pragma clang fp contract(off)
+      const float prod = sS32[j] * qv;
+      r = fmaxf(r - prod, 0.f);
+    }
+    return r;
+  };
+  // S = sum of r over the vocabulary (the strided order of the LDS kernel)
+  auto row_sum = [&]() {
+    double s = 0.0;
+    for (int v0 = tid; v0 < V; v0 += kStochBatch * kStochThreads) {
+      float pv[kStochBatch], qv[kStochBatch];
+#pragma unroll
+      for (int i = 0; i < kStochBatch; ++i) {
+        const int v = min(v0 + i * kStochThreads, V - 1);
+        pv[i] = pr[v];
+        qv[i] = q[v];
+      }
+#pragma unroll
+      for (int i = 0; i < kStochBatch; ++i)
+        if (v0 + i * kStochThreads < V) s += (double)r_of(pv[i], qv[i]);
+    }
+    return block_sum_f64(s, sred);
+  };
+  double S = row_sum();
+  while (true) {
+    if (tid < 64) {
+      const bool kid = tid >= 1 && tid < n && parent[row + tid] == u;
+      const uint64_t m = __ballot(kid);
+      if (kid) skids[__popcll(m & ((1ull << tid) - 1ull))] = tid;
+      if (tid == 0) snkids = __popcll(m);
+    }
+    __syncthreads();
+    const int nk = snkids;
+    bool moved = false;
+    for (int j = 0; j < nk; ++j) {
+      const int c = skids[j];
+      const int x = token[row + c];
+      const bool in_v = x >= 0 && x < V;
+      const float qx = in_v ? q[x] : 0.f;
+      const float rx = in_v ? r_of(pr[x], qx) : 0.f;
+      const bool pass = qx == 0.f ? rx > 0.f
+                                  : (double)u_accept[row + c] * S * (double)qx < (double)rx;
+      if (pass) {
+        if (tid == 0) schain[depth] = c;
+        u = c;
+        ++depth;
+        moved = true;
+        nrej = 0;
+        pr = p_target + (row + u) * V;
+        q = q_draft + (row + u) * V;
+        S = row_sum();
+        break;
+      }
+      __syncthreads();                                      // sS32[nrej] is free
+      if (tid == 0) sS32[nrej] = (float)S;
+      __syncthreads();
+      ++nrej;
+      S = row_sum();
+    }
+    if (!moved) break;
+    __syncthreads();                                        // skids reused
+  }
+
+  // bonus: the first v whose running sum of r passes u_bonus * S, over tiles of
+  // kStochScan * 1024 tokens (thread t owns kStochScan consecutive tokens of a tile);
+  // the scan stops at the first tile that holds it
+  const double target = (double)u_bonus[b] * S;
+  if (tid == 0) {
+    spick = V;
+    slastpos = -1;
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  double base = 0.0;
+  int lastpos = -1;
+  for (int t0 = 0; t0 < V; t0 += kStochScan * kStochThreads) {
+    const int v0 = t0 + tid * kStochScan;
+    float r[kStochScan];
+    double local = 0.0;
+#pragma unroll
+    for (int i = 0; i < kStochScan; ++i) {
+      const int v = min(v0 + i, V - 1);
+      r[i] = v0 + i < V ? r_of(pr[v], q[v]) : 0.f;
+      local += (double)r[i];
+      if (r[i] > 0.f) lastpos = v0 + i;
+    }
+    double incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) sscan[wave] = incl;
+    __syncthreads();
+    double before = base;
+    for (int w = 0; w < wave; ++w) before += sscan[w];
+    double run = before + incl - local;                     // sum of r below v0
+    if (run + local > target) {
+#pragma unroll
+      for (int i = 0; i < kStochScan; ++i) {
+        run += (double)r[i];
+        if (run > target && v0 + i < V) {
+          atomicMin(&spick, v0 + i);
+          break;
+        }
+      }
+    }
+    double tile = 0.0;
+    for (int w = 0; w < kStochThreads / 64; ++w) tile += sscan[w];
+    base += tile;
+    __syncthreads();                                        // spick settled, sscan reused
+    if (spick < V) break;
+  }
+  if (lastpos >= 0) atomicMax(&slastpos, lastpos);
+  __syncthreads();
+  if (tid == 0) {
+    int pick = spick;
+    if (pick >= V) pick = slastpos >= 0 ? slastpos : V - 1;
+    accept_len[b] = depth;
+    best_node[b] = u;
+    bonus_token[b] = pick;
+  }
+  if (path && tid < n_max) path[row + tid] = tid < depth ? schain[tid] : -1;
+}
+
 }  // namespace tv
 
 TV_API tv_status tree_accept_stochastic(int B, int n_max, int vocab, const int32_t* parent,
@@ -209,9 +375,13 @@ TV_API tv_status tree_accept_stochastic(int B, int n_max, int vocab, const int32
       !accept_len || !best_node || !bonus_token)
     return TV_ERR_NULL;
   if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || vocab < 1) return TV_ERR_SHAPE;
-  if (vocab > tv::kStochMaxVocab) return TV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(tv::accept_stochastic_kernel, dim3(B), dim3(tv::kStochThreads), 0, stream,
-                     n_max, vocab, parent, anc, n_nodes, token, p_target, q_draft, u_accept,
-                     u_bonus, accept_len, best_node, bonus_token, path);
+  if (vocab <= tv::kStochMaxVocab)
+    hipLaunchKernelGGL(tv::accept_stochastic_kernel, dim3(B), dim3(tv::kStochThreads), 0, stream,
+                       n_max, vocab, parent, anc, n_nodes, token, p_target, q_draft, u_accept,
+                       u_bonus, accept_len, best_node, bonus_token, path);
+  else
+    hipLaunchKernelGGL(tv::accept_stochastic_stream_kernel, dim3(B), dim3(tv::kStochThreads), 0,
+                       stream, n_max, vocab, parent, anc, n_nodes, token, p_target, q_draft,
+                       u_accept, u_bonus, accept_len, best_node, bonus_token, path);
   return tv::launch_status();
 }
