@@ -187,6 +187,27 @@ tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C, const 
                                 int32_t* cand, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * tree_cost_lookup -- the verification cost at one (batch, context) from a calibrated
+ * table (HOST pointers, no device work).  [EAGLE-4] "verification trees and the
+ * harness": a one-time calibration records verification latency against batch size,
+ * context length and candidate count, and the harness reads its costs from it.
+ *   batch [n_batch], context [n_context], nodes [n_nodes_pts]: ascending grid axes
+ *              (batch and context >= 1; node counts in 1..64)
+ *   cost_us    [n_batch][n_context][n_nodes_pts]: measured microseconds (> 0, finite)
+ *              of one tree_verify_attn call at each grid point
+ *   B, L       the caller's batch and context length; n_max <= 64
+ *   cost_out   [n_max] out: cost_out[N-1] = the latency with N nodes per tree: log
+ *              latency bilinear in (log batch, log context) (exact for power laws),
+ *              latency linear in N, the nearest grid value outside the grid, and
+ *              never falling as N grows
+ * Feeds tree_budget_thresholds.  Errors: TV_ERR_NULL, TV_ERR_SHAPE (empty or
+ * non-ascending axes, sizes out of range, a latency that is not positive and finite).
+ */
+tv_status tree_cost_lookup(const int32_t* batch, int n_batch, const int32_t* context,
+                           int n_context, const int32_t* nodes, int n_nodes_pts,
+                           const float* cost_us, int B, int L, int n_max, float* cost_out);
+
+/*
  * tree_budget_thresholds -- the per-place bars of the verify budget (HOST pointers,
  * no device work).  [EAGLE-4] "verification trees and the harness": a calibrated cost
  * table (verification latency against batch, context length and candidate count)

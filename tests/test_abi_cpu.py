@@ -189,6 +189,44 @@ def test_attn_plan(L):
     assert L.tree_verify_attn_plan(1, 1, 64, 32, 8, 128, 100, None) == NULL
 
 
+def test_cost_lookup_closed_forms(L):
+    """tree_cost_lookup: exact on a power law in batch and context at and between grid
+    points, linear in N between node points, the nearest grid value outside the grid,
+    never falling with N; malformed tables rejected."""
+    import numpy as np
+    Bs, Ls, Ns = [1, 4, 16], [1024, 4096, 32768], [1, 16, 64]
+    law = lambda b, l, n: 2.5 * b ** 0.7 * l ** 0.9 * (1 + n / 32)
+    c = np.array([[[law(b, l, n) for n in Ns] for l in Ls] for b in Bs], np.float32)
+    for (b, l) in [(1, 1024), (4, 4096), (2, 2048), (8, 20000), (16, 32768)]:
+        got = tv.cost_lookup(Bs, Ls, Ns, c, b, l)
+        want = np.array([law(b, l, n) for n in (1, 16, 64)])
+        assert np.allclose(got[[0, 15, 63]], want, rtol=2e-6), (b, l)
+        mid = [law(b, l, 1) + (law(b, l, 16) - law(b, l, 1)) * (n - 1) / 15 for n in (5, 9)]
+        assert np.allclose(got[[4, 8]], mid, rtol=2e-6)
+    # outside the grid: the nearest grid value
+    assert np.array_equal(tv.cost_lookup(Bs, Ls, Ns, c, 64, 100000), tv.cost_lookup(Bs, Ls, Ns, c, 16, 32768))
+    assert np.array_equal(tv.cost_lookup(Bs, Ls, Ns, c, 1, 10), tv.cost_lookup(Bs, Ls, Ns, c, 1, 1024))
+    # a measured dip in N is lifted to the running maximum
+    d = c.copy()
+    d[:, :, 1] = d[:, :, 0] * 0.5
+    got = tv.cost_lookup(Bs, Ls, Ns, d, 4, 4096)
+    assert np.all(np.diff(got) >= 0) and got[15] == got[0]
+    out = np.empty(64, np.float32)
+
+    def call(b, l, n, cc):
+        arrs = [np.ascontiguousarray(a, np.int32) for a in (b, l, n)] + [np.ascontiguousarray(cc, np.float32)]
+        return L.tree_cost_lookup(arrs[0].ctypes.data, len(b), arrs[1].ctypes.data, len(l),
+                                  arrs[2].ctypes.data, len(n), arrs[3].ctypes.data, 4, 4096, 64,
+                                  out.ctypes.data)
+    assert call(Bs, Ls, Ns, c) == OK
+    assert call([4, 1, 16], Ls, Ns, c) == SHAPE                              # not ascending
+    assert call(Bs, Ls, [1, 16, 65], c) == SHAPE                             # past 64 nodes
+    bad = c.copy()
+    bad[1, 1, 1] = 0.0
+    assert call(Bs, Ls, Ns, bad) == SHAPE                                    # not positive
+    assert L.tree_cost_lookup(Z, 3, Z, 3, Z, 3, Z, 4, 4096, 64, Z) == NULL
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libtreeverify.so")
@@ -236,7 +274,7 @@ def test_accept_stochastic_validation(L):
     assert _stoch(L, B=0) == SHAPE
     assert _stoch(L, n_max=65) == SHAPE
     assert _stoch(L, V=0) == SHAPE
-    assert _stoch(L, V=36865) == UNSUP
+    assert _stoch(L, V=-5) == SHAPE
 
 
 def test_budget_thresholds(L):

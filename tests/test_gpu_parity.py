@@ -818,6 +818,36 @@ def test_draft_tree_stops_without_changing_the_tree(wid):
     assert out.score.cpu().numpy().tobytes() == ref.score.tobytes()
 
 
+# ----------------------------------------------------------------------------- cost table
+
+def test_cost_table_measure_and_lookup():
+    """The calibration measures this library's own tree_verify_attn over a batch x context
+    x node-count grid: latency grows with the node count where verification is MFMA-bound
+    (4 x 16384 keys, 512 query rows per KV head at 64 nodes), a second measurement agrees
+    within 15%, the lookup returns the measured (running-maximum) row at grid points, and
+    calibrate() at one point gives the same bars as the table there."""
+    from tree_attention_verify_ancestor_amd import harness
+    kw = dict(batch=(1, 4), context=(2048, 16384), nodes=(1, 16, 32, 64), reps=5)
+    t1 = harness.CostTable.measure(64, 8, **kw)
+    t2 = harness.CostTable.measure(64, 8, **kw)
+    c1, c2 = t1.cost_us, t2.cost_us
+    assert np.all(c1 > 0) and np.all(np.abs(c1 - c2) <= 0.15 * np.maximum(c1, c2)), (c1, c2)
+    assert c1[1, 1, 3] > 1.5 * c1[1, 1, 0], c1[1, 1]              # MFMA-bound: nodes cost
+    for i, B in enumerate(kw["batch"]):
+        for j, L in enumerate(kw["context"]):
+            got = t1.cost(B, L)
+            assert np.all(np.diff(got) >= 0)
+            want = np.maximum.accumulate(c1[i, j])
+            assert np.array_equal(got[[0, 15, 31, 63]], want.astype(np.float32)), (B, L)
+    bars = t1.budget_log(4, 16384, 1e-4)
+    assert np.array_equal(bars, tv.budget_thresholds(t1.cost(4, 16384), 1e-4))
+    one = harness.calibrate(4, 16384, 64, 8, n_points=kw["nodes"], reps=5)
+    assert np.all(np.diff(one) >= 0) and one.shape == (64,)
+    assert np.all(np.abs(one[[0, 63]] - t1.cost(4, 16384)[[0, 63]]) <= 0.15 * one[[0, 63]])
+    j = harness.CostTable.from_json(t1.to_json())
+    assert np.allclose(j.cost(2, 5000), t1.cost(2, 5000), rtol=1e-3)
+
+
 # ----------------------------------------------------------------------------- low-rank candidate head
 
 def _cand_inputs(seed, rows, d, r, V):

@@ -15,9 +15,10 @@ from .ops import (abi_version, tree_build, expand_workspace, ExpandOutputs, tree
                   attn_workspace, attn_plan, tree_verify_attn, tree_verify_attn_noalloc,
                   tree_accept, tree_kv_compact,
                   tree_accept_stochastic, tree_draft_continue, tree_candidate_logits,
-                  budget_thresholds)
+                  budget_thresholds, cost_lookup)
 
 __all__ = ["TreeVerifyError", "lib", "EXPORTS", "LIB_PATH", "abi_version", "tree_build",
            "expand_workspace", "ExpandOutputs", "tree_expand_rerank", "attn_workspace", "attn_plan",
            "tree_verify_attn", "tree_verify_attn_noalloc", "tree_accept", "tree_kv_compact", "tree_accept_stochastic",
-           "tree_draft_continue", "tree_candidate_logits", "budget_thresholds"]
+           "tree_draft_continue", "tree_candidate_logits", "budget_thresholds",
+           "cost_lookup"]

@@ -11,7 +11,7 @@ STATUS_NAMES = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_DTYP
 TV_F32, TV_BF16 = 0, 1
 
 EXPORTS = ("tv_abi_version", "tv_status_string", "tree_build", "tree_expand_workspace_size",
-           "tree_expand_rerank", "tree_draft_continue", "tree_budget_thresholds",
+           "tree_expand_rerank", "tree_draft_continue", "tree_cost_lookup", "tree_budget_thresholds",
            "tree_verify_attn_workspace_size", "tree_verify_attn_plan", "tree_verify_attn",
            "tree_verify_attn_noalloc",
            "tree_accept", "tree_accept_stochastic", "tree_kv_compact",
@@ -30,6 +30,7 @@ _SIGNATURES = {
     "tree_expand_rerank": (_I, [_P, _S, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P,
                                 _P, _P, _P, _P]),
     "tree_draft_continue": (_I, [_P, _S, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "tree_cost_lookup": (_I, [_P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
     "tree_budget_thresholds": (_I, [_P, _I, _F, _P]),
     "tree_verify_attn_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "tree_verify_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),

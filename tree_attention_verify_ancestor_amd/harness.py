@@ -1,50 +1,53 @@
-"""Cost table for the verify budget: tree_verify_attn latency against the node count.
+"""Cost table for the verify budget: tree_verify_attn latency against batch, context
+length and node count.
 
 "Technical analysis of EAGLE-4", section "EAGLE-4 verification trees and the
 harness": before serving, a one-time calibration on the target GPU builds a table of
 verification latency against batch size, context length and candidate count; the
 harness then adds candidates while the gain in cumulative probability per unit of
 marginal cost stays above a threshold, and stops drafting once it falls below.
-calibrate() measures this library's own tree_verify_attn (HIP events around graph
-replays) at one (batch, context) for a few node counts and interpolates the rest; budget_thresholds() (the library's host
-helper) turns the table into the per-place bars tree_expand_rerank takes;
-draft_tree() drafts level by level and stops with tree_draft_continue.
 
-Usage: python -m tree_attention_verify_ancestor_amd.harness   (prints JSON tables)
+CostTable.measure() times this library's own tree_verify_attn (bf16, chain trees, HIP
+events around graph replays) over a grid of batch sizes, context lengths and node
+counts.  CostTable.cost(B, L) reads the latency of N = 1..64 nodes at the caller's
+batch and context through the library's host helper tree_cost_lookup (interpolation
+in log batch and log context, linear in N); budget_log() turns that into the
+per-place bars tree_expand_rerank takes (tree_budget_thresholds); draft_tree() drafts
+level by level and stops with tree_draft_continue.
+
+Usage: python -m tree_attention_verify_ancestor_amd.harness [out.json]
 """
 
 import json
+import sys
 
 import numpy as np
 import torch
 
 from . import ops
 
-DEFAULT_N = (1, 4, 8, 16, 24, 32, 40, 48, 56, 64)
+GRID_BATCH = (1, 4, 16, 32)
+GRID_CONTEXT = (1024, 4096, 16384, 32768)
+GRID_NODES = (1, 8, 16, 24, 32, 48, 64)
 
 
-def calibrate(B, L, Hq, Hkv, D=128, n_points=DEFAULT_N, reps=20, device="cuda", seed=0):
-    """Returns float32 cost_us[64]: cost_us[N-1] = microseconds of one bf16
-    tree_verify_attn call with N nodes per tree (chains), prefix L per sequence."""
-    g = torch.Generator(device=device).manual_seed(seed)
+def _time_calls(Hq, Hkv, D, B, L, nodes, bufs, reps, device):
+    """Microseconds of one call at each node count (graph replays of reps calls)."""
+    q, kt, vt, kp, vp = bufs
     n_max = 64
-    bf = dict(dtype=torch.bfloat16, device=device)
-    q = (torch.randn((B, n_max, Hq, D), generator=g, device=device) * 0.5).to(torch.bfloat16)
-    kt = (torch.randn((B, n_max, Hkv, D), generator=g, device=device) * 0.5).to(torch.bfloat16)
-    vt = (torch.randn((B, n_max, Hkv, D), generator=g, device=device) * 0.5).to(torch.bfloat16)
-    kp = (torch.randn((B * L, Hkv, D), generator=g, device=device) * 0.5).to(torch.bfloat16)
-    vp = (torch.randn((B * L, Hkv, D), generator=g, device=device) * 0.5).to(torch.bfloat16)
+    qb, ktb, vtb = q[:B], kt[:B], vt[:B]
+    kpb, vpb = kp[:B * L], vp[:B * L]
     offs = torch.arange(B + 1, dtype=torch.int64, device=device) * L
     parent = torch.full((B, n_max), -1, dtype=torch.int32, device=device)
     parent[:, 1:] = torch.arange(n_max - 1, dtype=torch.int32, device=device)
     ws = ops.attn_workspace(torch.bfloat16, B, n_max, Hq, Hkv, D, L, device)
-    out = torch.empty((B, n_max, Hq, D), **bf)
-    meas = []
-    for n in n_points:
+    out = torch.empty((B, n_max, Hq, D), dtype=torch.bfloat16, device=device)
+    res = []
+    for n in nodes:
         nn = torch.full((B,), n, dtype=torch.int32, device=device)
         anc, _, _, _ = ops.tree_build(parent, nn)
-        call = lambda: ops.tree_verify_attn(q, kt, vt, kp, vp, offs, nn, anc, L, out=out, ws=ws,
-                                            want_lse=False)
+        call = lambda: ops.tree_verify_attn(qb, ktb, vtb, kpb, vpb, offs, nn, anc, L, out=out,
+                                            ws=ws, want_lse=False)
         call()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -59,9 +62,64 @@ def calibrate(B, L, Hq, Hkv, D=128, n_points=DEFAULT_N, reps=20, device="cuda", 
             graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        meas.append(e0.elapsed_time(e1) * 1e3 / (3 * reps))
-    cost = np.interp(np.arange(1, n_max + 1), np.asarray(n_points, float), np.asarray(meas))
-    return np.maximum.accumulate(cost).astype(np.float32)      # latency never falls with N
+        res.append(e0.elapsed_time(e1) * 1e3 / (3 * reps))
+    return res
+
+
+def _buffers(Hq, Hkv, D, B, L, device, seed):
+    g = torch.Generator(device=device).manual_seed(seed)
+    r = lambda shape: (torch.randn(shape, generator=g, device=device) * 0.5).to(torch.bfloat16)
+    return (r((B, 64, Hq, D)), r((B, 64, Hkv, D)), r((B, 64, Hkv, D)), r((B * L, Hkv, D)),
+            r((B * L, Hkv, D)))
+
+
+class CostTable:
+    """Latency of tree_verify_attn over a grid: cost_us[i][j][k] microseconds at batch
+    batch[i], context context[j] and nodes[k] nodes per tree, for one head shape."""
+
+    def __init__(self, batch, context, nodes, cost_us, Hq, Hkv, D=128):
+        self.batch, self.context, self.nodes = tuple(batch), tuple(context), tuple(nodes)
+        self.cost_us = np.asarray(cost_us, dtype=np.float32)
+        self.Hq, self.Hkv, self.D = Hq, Hkv, D
+
+    @classmethod
+    def measure(cls, Hq, Hkv, D=128, batch=GRID_BATCH, context=GRID_CONTEXT, nodes=GRID_NODES,
+                reps=10, device="cuda", seed=0):
+        """Time every grid point on the device (one set of buffers of the largest size)."""
+        bufs = _buffers(Hq, Hkv, D, max(batch), max(context), device, seed)
+        cost = np.zeros((len(batch), len(context), len(nodes)), np.float32)
+        for i, B in enumerate(batch):
+            for j, L in enumerate(context):
+                cost[i, j] = _time_calls(Hq, Hkv, D, B, L, nodes, bufs, reps, device)
+        del bufs
+        return cls(batch, context, nodes, cost, Hq, Hkv, D)
+
+    def cost(self, B, L, n_max=64):
+        """float32 [n_max]: latency with N = 1..n_max nodes at batch B and context L."""
+        return ops.cost_lookup(self.batch, self.context, self.nodes, self.cost_us, B, L, n_max)
+
+    def budget_log(self, B, L, threshold, n_max=64):
+        """The verify budget's bars at batch B and context L (tree_budget_thresholds)."""
+        return ops.budget_thresholds(self.cost(B, L, n_max), threshold)
+
+    def to_json(self):
+        return {"Hq": self.Hq, "Hkv": self.Hkv, "D": self.D, "batch": list(self.batch),
+                "context": list(self.context), "nodes": list(self.nodes),
+                "cost_us": [[[round(float(x), 3) for x in r] for r in p] for p in self.cost_us]}
+
+    @classmethod
+    def from_json(cls, d):
+        return cls(d["batch"], d["context"], d["nodes"], d["cost_us"], d["Hq"], d["Hkv"], d["D"])
+
+
+def calibrate(B, L, Hq, Hkv, D=128, n_points=GRID_NODES, reps=20, device="cuda", seed=0):
+    """float32 cost_us[64] at one (batch, context): the node points measured on the
+    device, the rest read through tree_cost_lookup (a one-point batch / context grid)."""
+    bufs = _buffers(Hq, Hkv, D, B, L, device, seed)
+    meas = _time_calls(Hq, Hkv, D, B, L, n_points, bufs, reps, device)
+    del bufs
+    return ops.cost_lookup([B], [max(L, 1)], n_points, np.asarray(meas, np.float32)[None, None, :],
+                           B, L)
 
 
 def budget_thresholds(cost_us, threshold):
@@ -99,13 +157,14 @@ def draft_tree(level_logits, B, k, max_steps, m=0, m_per_seq=None, budget_log=No
 
 
 def _main():
-    shapes = {"B1_L2048_mha32": (1, 2048, 32, 32), "B1_L4096_gqa32x8": (1, 4096, 32, 8),
-              "B4_L32768_gqa64x8": (4, 32768, 64, 8), "B32_L4352_gqa32x8": (32, 4352, 32, 8)}
-    res = {}
-    for name, (B, L, Hq, Hkv) in shapes.items():
-        c = calibrate(B, L, Hq, Hkv)
-        res[name] = {"cost_us": [round(float(x), 2) for x in c]}
-        print(json.dumps({name: res[name]}), flush=True)
+    """Measure the grid for the head shapes of the studied workloads and print it as JSON
+    (to the file named on the command line as well)."""
+    tables = {}
+    for name, (Hq, Hkv) in {"mha32": (32, 32), "gqa32x8": (32, 8), "gqa64x8": (64, 8)}.items():
+        tables[name] = CostTable.measure(Hq, Hkv).to_json()
+        print(json.dumps({name: tables[name]}), flush=True)
+    if len(sys.argv) > 1:
+        json.dump(tables, open(sys.argv[1], "w"), indent=1)
 
 
 if __name__ == "__main__":

@@ -160,6 +160,22 @@ def budget_thresholds(cost_us, threshold):
     return out
 
 
+def cost_lookup(batch, context, nodes, cost_us, B, L, n_max=64):
+    """Latency [n_max] (host float32) at batch B and context L from a cost table measured
+    over the grid batch x context x nodes (cost_us float32 [len(batch)][len(context)]
+    [len(nodes)]); the interpolation is the library's host helper."""
+    import numpy as np
+    ax = [np.ascontiguousarray(a, dtype=np.int32) for a in (batch, context, nodes)]
+    c = np.ascontiguousarray(cost_us, dtype=np.float32)
+    if c.shape != tuple(len(a) for a in ax):
+        raise ValueError(f"cost table shape {c.shape} does not match the axes")
+    out = np.empty(n_max, dtype=np.float32)
+    check("tree_cost_lookup", lib().tree_cost_lookup(
+        ax[0].ctypes.data, len(ax[0]), ax[1].ctypes.data, len(ax[1]), ax[2].ctypes.data,
+        len(ax[2]), c.ctypes.data, int(B), int(L), int(n_max), out.ctypes.data))
+    return out
+
+
 def attn_workspace(dtype, B, n_max, Hq, Hkv, D, max_prefix_len, device="cuda"):
     n = lib().tree_verify_attn_workspace_size(_DT[dtype], B, n_max, Hq, Hkv, D, max_prefix_len)
     return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
