@@ -55,19 +55,25 @@ class TreeVerifyError(RuntimeError):
         super().__init__(f"{fn} returned {STATUS_NAMES.get(code, code)}")
 
 
+def load(path):
+    """A build of the library at `path` with the C signatures set (loaded RTLD_LOCAL, so
+    several builds can live in one process)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m tree_attention_verify_ancestor_amd.build`")
+    handle = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
     """The loaded library.  Raises when it has not been built: there is no fallback."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing; build it with "
-                              "`python -m tree_attention_verify_ancestor_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
 
 

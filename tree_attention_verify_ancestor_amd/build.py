@@ -21,17 +21,29 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose=False):
-    """Compile every HIP source into the in-tree shared library; returns its path."""
+# the same sources with TV_PLAN_VARIANT=1: another work partition and order, the same
+# results (tests compare the two builds bit for bit)
+LIB_VARIANT = os.path.join(PKG, "libtreeverify_variant.so")
+
+
+def _compile(out, extra, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stderr[-8000:])
-    os.replace(tmp, LIB)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), tmp, out
+
+
+def build(verbose=False):
+    """Compile every HIP source into the in-tree shared library (and its plan-variant
+    twin); returns the library's path."""
+    jobs = [_compile(LIB, [], verbose), _compile(LIB_VARIANT, ["-DTV_PLAN_VARIANT=1"], verbose)]
+    for proc, tmp, out in jobs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + err[-8000:])
+        os.replace(tmp, out)
     return LIB
 
 

@@ -123,7 +123,7 @@ static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_pref
   p.chunk_keys = (int)ck;
   p.n_chunks = max_prefix > 0 ? (int)((max_prefix + ck - 1) / ck) : 1;
   p.total_wgs = p.units * p.n_chunks;
-  p.grid = (p.total_wgs + 7) / 8 * 8;
+  p.grid = (p.total_wgs + 7) / 8 * 8 + (kPlanVariant ? 64 : 0);
   const size_t slots = (size_t)p.units * p.n_chunks * p.rows_per_wg;
   p.part_o_bytes = slots * D * 4;
   p.part_ml_bytes = slots * 8;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       s_work[j] = w;
     }
     __syncthreads();
-    by_work = *s_ragged != 0;
+    by_work = kPlanVariant || *s_ragged != 0;
     if (by_work) {
       const int place = x / per;
       for (int j = threadIdx.x; j < P; j += blockDim.x) {
@@ -1202,7 +1202,7 @@ static void launch_bf16(const AttnPlan& p, const AttnArgs& a, hipStream_t stream
   else hipLaunchKernelGGL((attn_bf16<D, 8, 1, 1>), grid, block, 0, stream, a);
   if (p.n_chunks > 1) {
     const int rows = a.B * a.n_max * a.Hq;
-    if (rows <= kCombineFewRows)
+    if ((rows <= kCombineFewRows) != kPlanVariant)
       hipLaunchKernelGGL((attn_combine<D, 4>), dim3((rows + 3) / 4), dim3(kCombineLanes * 4), 0, stream, a);
     else
       hipLaunchKernelGGL((attn_combine<D, 8>), dim3((rows + 7) / 8), dim3(kCombineLanes * 8), 0, stream, a);
@@ -1241,7 +1241,7 @@ static void* scratch_of_current_device() {
 
 TV_API size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int Hq, int Hkv,
                                               int D, int max_prefix_len) {
-  if (dt != TV_BF16) return 0;
+  if (!tv::known_dtype(dt) || dt != TV_BF16) return 0;
   if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
       max_prefix_len < 0 || (D != 64 && D != 128))
     return 0;
@@ -1250,7 +1250,7 @@ TV_API size_t tree_verify_attn_workspace_size(tv_dtype dt, int B, int n_max, int
 
 TV_API tv_status tree_verify_attn_plan(tv_dtype dt, int B, int n_max, int Hq, int Hkv, int D,
                                        int max_prefix_len, int32_t* plan) {
-  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_DTYPE;
+  if (!tv::known_dtype(dt)) return TV_ERR_DTYPE;
   if (!plan) return TV_ERR_NULL;
   if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
       max_prefix_len < 0 || D < 1)
@@ -1270,7 +1270,7 @@ TV_API tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, in
                                   const int32_t* n_nodes, const uint64_t* anc, void* out,
                                   float* lse, void* ws, size_t ws_bytes, int32_t* seq_status,
                                   hipStream_t stream) {
-  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_DTYPE;
+  if (!tv::known_dtype(dt)) return TV_ERR_DTYPE;
   if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
       max_prefix_len < 0 || D < 1)
     return TV_ERR_SHAPE;
@@ -1319,7 +1319,8 @@ TV_API tv_status tree_verify_attn(tv_dtype dt, int B, int Hq, int Hkv, int D, in
   a.n_rb = p.n_rb;
   a.total_wgs = p.total_wgs;
   // ranking pays where many sequences of different lengths share the GPU
-  a.rank_pairs = B >= tv::kRankMinBatch && (long)B * p.n_chunks <= tv::kMaxRankPairs;
+  a.rank_pairs = B >= (tv::kPlanVariant ? 2 : tv::kRankMinBatch) &&
+                 (long)B * p.n_chunks <= tv::kMaxRankPairs;
   a.sl2 = scale * tv::kLog2e;
   if (D == 128) tv::launch_bf16<128>(p, a, stream);
   else tv::launch_bf16<64>(p, a, stream);

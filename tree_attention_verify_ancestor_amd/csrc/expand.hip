@@ -701,7 +701,8 @@ struct RowPlan {
 };
 static RowPlan row_plan(int B, int rows, int vocab) {
   const long units = (long)B * rows;
-  const long want = (1024 + units - 1) / units;
+  const long target = kPlanVariant ? 256 : 1024;
+  const long want = (target + units - 1) / units;
   const long lo = (vocab + 8191) / 8192;
   const long hi = (vocab + 1023) / 1024;
   long n = want < hi ? want : hi;

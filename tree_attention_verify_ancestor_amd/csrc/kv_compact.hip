@@ -41,7 +41,7 @@ TV_API tv_status tree_kv_compact(tv_dtype dt, int B, int n_max, int Hkv, int D, 
                                  const void* v_tree, const int32_t* path,
                                  const int32_t* accept_len, void* k_dst, void* v_dst,
                                  const int64_t* dst_row, int64_t dst_rows, hipStream_t stream) {
-  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_DTYPE;
+  if (!tv::known_dtype(dt)) return TV_ERR_DTYPE;
   if (B < 1 || n_max < 1 || n_max > TV_MAX_NODES || Hkv < 1 || D < 1 || dst_rows < 0)
     return TV_ERR_SHAPE;
   if (!k_tree || !v_tree || !path || !accept_len || !dst_row) return TV_ERR_NULL;

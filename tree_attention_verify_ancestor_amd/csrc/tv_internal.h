@@ -8,8 +8,19 @@
 
 #define TV_API extern "C" __attribute__((visibility("default")))
 
+// A second build of the library (TV_PLAN_VARIANT=1) partitions and orders the work
+// differently without changing any result: attention takes the ranked (sequence,
+// chunk) order for every batch of two or more, pads its grid with idle workgroups and
+// groups its merge rows the other way; expansion splits each logit row into chunks
+// four times larger.  Tests demand bit-identical outputs from both builds, which an
+// LDS race or an order-dependent reduction would break.
+#ifndef TV_PLAN_VARIANT
+#define TV_PLAN_VARIANT 0
+#endif
+
 namespace tv {
 
+constexpr bool kPlanVariant = TV_PLAN_VARIANT != 0;
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -37,6 +48,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = w > v ? w : v;
   }
   return v;
+}
+
+// A dtype argument is one of the two the ABI names.  Its bits are read as an int: a C
+// caller may pass any value, and an enum value outside the enumeration must not be
+// used as one.
+inline bool known_dtype(tv_dtype dt) {
+  int v;
+  __builtin_memcpy(&v, &dt, sizeof v);
+  return v == TV_F32 || v == TV_BF16;
 }
 
 // Host-side launch check.
