@@ -136,6 +136,8 @@ SMALL_EXPAND = [  # (B, k, S, V, m, quantised)
     # rows split over many chunks: ties across lanes, waves and chunks; odd vocab sizes
     (2, 10, 3, 50000, 40, True), (3, 4, 3, 20001, 16, True), (1, 16, 2, 9001, 64, False),
     (1, 2, 2, 600000, 4, True), (1, 3, 2, 600001, 5, False),
+    # fewer lanes hold logits than k: every logit of the chunk is a candidate
+    (2, 8, 3, 16, 20, False), (2, 16, 2, 40, 30, False),
 ]
 
 

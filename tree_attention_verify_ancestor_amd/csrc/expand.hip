@@ -22,8 +22,12 @@
 // Workspace per sequence: a header {status, pool count, next step, frontier slots and
 // scores}, the pool of {parent slot, token, score, depth} records in creation order,
 // then one record per (frontier row, chunk).
+#include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
+#include "exp64.h"
 #include "tv_internal.h"
 
 namespace tv {
@@ -153,8 +157,84 @@ __device__ __forceinline__ void best_two(const float (&x)[EPT], float after_v, i
   }
 }
 
+// float64 sum over the wave by DPP within rows of 16 lanes, then the four row sums
+// (every lane gets the same value)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_f64<0xB1>(v);     // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);     // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);    // row_half_mirror: the 8-lane sum
+  v += dpp_f64<0x140>(v);    // row_mirror: the 16-lane sum
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// A lower bound on the k-th largest of the wave's keys (NS per lane; 0 marks no key):
+// the largest T whose low 32 - BITS bits are 0 with at least k keys at or above it,
+// found bit by bit from the top (BITS = 32: the k-th largest key itself).  0 when
+// fewer than k keys are nonzero.
+template <int NS, int BITS>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[NS], int k) {
+  uint32_t T = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 32 - BITS; --bit) {
+    const uint32_t c = T | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) n += __popcll(__ballot(key[q] >= c));
+    if (n >= k) T = c;
+  }
+  return T;
+}
+
+// An entry's rank key: larger value first, then lower id (ids >= 0)
+__device__ __forceinline__ uint64_t rank_key(float v, int id) {
+  return ((uint64_t)fkey(v) << 32) | (uint32_t)~id;
+}
+// the float a key was made from (+0 for -0)
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+// How many of keys[0..n) (in LDS) are larger than key.  Every lane reads the same
+// address at a time (a broadcast), eight reads in flight, and compares in its own
+// registers: no cross-lane or scalar step in the loop.
+__device__ __forceinline__ int lds_rank_desc(const uint64_t* keys, int n, uint64_t key) {
+  int rk = 0;
+#pragma unroll 8
+  for (int o = 0; o < n; ++o) rk += (int)(keys[o] > key);
+  return rk;
+}
+__device__ __forceinline__ float key_float(uint64_t key) { return key_value((uint32_t)(key >> 32)); }
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+constexpr int kCandW = 64;               // threshold candidates kept per wave
+
+// One chunk of one logit row per workgroup.  Each lane holds EPT logits; the chunk's
+// maximum, its float64 sum of exp(l - max) and its top-k (value descending, id
+// ascending) are recorded for expand_select_kernel.
+//   sum   each lane sums exp(l - its own maximum) with exp_nonpos, then rescales by
+//         exp(lane max - chunk max).  A NaN or infinite logit makes its lane's sum NaN,
+//         which flags the chunk.
+//   top-k T = the largest, over the waves, of the k-th largest lane maximum of a wave:
+//         at least k logits of the chunk are >= T, so its top-k is among them.  Those
+//         few (ballot-compacted per wave into LDS) are ranked by one wave across lanes.
+//         When a wave gathers more than kCandW (heavy ties), the exact per-wave
+//         selection rounds below run instead.
+// Five waves per SIMD fit (EPT <= 32): a level's ~1280 workgroups are then resident at once.
 template <int EPT, bool VEC>
-__global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(EPT >= 64 ? 4 : 5)))
+void expand_rows_kernel(
     char* __restrict__ ws, size_t stride, size_t rec_off, int k, int step, int rows, int vocab,
     int chunk, const float* __restrict__ logits) {
   const int c = blockIdx.x;
@@ -165,6 +245,12 @@ __global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
   if (step > 1 && (hdr->status != TV_SEQ_OK || hdr->next_step != step)) return;
   ChunkRec* rec = (ChunkRec*)(seq + rec_off) + (size_t)r * kMaxRowChunks + c;
 
+  __shared__ double s_tab[kChunkWaves][kExpTab];
+  __shared__ float s_cv[kChunkWaves][kCandW];
+  __shared__ int s_ci[kChunkWaves][kCandW];
+  __shared__ uint64_t s_ck[kWave];
+  __shared__ uint32_t s_thr[kChunkWaves];
+  __shared__ int s_cnt[kChunkWaves];
   __shared__ float s_wv[kChunkWaves][kTopKMax];
   __shared__ int s_wi[kChunkWaves][kTopKMax];
   __shared__ float s_max[kChunkWaves];
@@ -174,6 +260,12 @@ __global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  // each wave its own copy of the exp table, written from immediates (no memory read
+  // ahead of the logit loads) and read by the same wave only: no barrier
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < kExpTab; ++i) s_tab[wave][i] = kExp2Frac64[i];
+  }
   const float* row = logits + ((size_t)b * rows + r) * (size_t)vocab;
   const int e0 = c * chunk;
   const int e1 = min(vocab, e0 + chunk);
@@ -182,8 +274,8 @@ __global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
     return VEC ? e0 + 4 * (tid + kChunkThreads * (j >> 2)) + (j & 3) : e0 + tid + kChunkThreads * j;
   };
 
-  // every load is issued before any is used (addresses clamped into the chunk, values
-  // past its end replaced by -inf afterwards), so they are all in flight together
+  // every load is issued before any is used (addresses clamped into the chunk), so
+  // they are all in flight together
   float x[EPT];
   if constexpr (VEC) {
 #pragma unroll
@@ -199,110 +291,287 @@ __global__ __launch_bounds__(kChunkThreads) void expand_rows_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) x[j] = row[min(id_of(j), e1 - 1)];
   }
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const bool in = id_of(j) < e1;
-    bad |= in && !isfinite(x[j]);
-    x[j] = in ? x[j] : -INFINITY;
-  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const double* tab = s_tab[wave];
 
-  float mx = -INFINITY;
+  // a chunk of exactly EPT logits per thread needs no bounds tests (every chunk of a
+  // row but its last)
+  auto body = [&](auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    auto in = [&](int j) { return !TAIL || id_of(j) < e1; };
+    // logits past the chunk become -FLT_MAX: finite, never a candidate, summed as 0
+    if constexpr (TAIL) {
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) mx = fmaxf(mx, x[j]);
-  float h1v, h2v;
-  int h1j, h2j;
-  best_two(x, INFINITY, -1, h1v, h1j, h2v, h2j);
-
-  // this wave's top-k: k rounds over the lanes' heads.  A lane keeps its best two; when
-  // it wins with its second already promoted, it rescans for the two after the winner.
-  bool second_known = true;
-  for (int t = 0; t < k; ++t) {
-    const int win = wave_argbest(h1j < EPT ? fkey(h1v) : 0u, id_of(h1j));
-    if (win < 0) {
-      if (lane == 0) {
-        s_wv[wave][t] = -INFINITY;
-        s_wi[wave][t] = INT32_MAX;
-      }
-      continue;
+      for (int j = 0; j < EPT; ++j) x[j] = in(j) ? x[j] : -FLT_MAX;
     }
-    if (lane == win) {
-      s_wv[wave][t] = h1v;
-      s_wi[wave][t] = id_of(h1j);
-      if (second_known) {
-        h1v = h2v;
-        h1j = h2j;
-        second_known = false;
-      } else {
-        float a1v, a2v;
-        int a1j, a2j;
-        best_two(x, h1v, h1j, a1v, a1j, a2v, a2j);
-        h1v = a1v;
-        h1j = a1j;
-        h2v = a2v;
-        h2j = a2j;
-        second_known = true;
-      }
-    }
-  }
-
-  const float wm = wave_max_f32(mx);
-  const bool wbad = __ballot(bad) != 0ull;
-  if (lane == 0) {
-    s_max[wave] = wm;
-    s_bad[wave] = wbad;
-  }
-  __syncthreads();
-  float M = s_max[0];
-  int anybad = s_bad[0];
+    const bool has = in(0);
+    float ml = -FLT_MAX;
 #pragma unroll
-  for (int w = 1; w < kChunkWaves; ++w) {
-    M = fmaxf(M, s_max[w]);
-    anybad |= s_bad[w];
-  }
-  if (anybad) {
-    if (tid == 0) rec->bad = 1;
-    return;
-  }
-
-  // float64 sum of exp(l - chunk max); elements past the chunk are -inf and add 0
-  const double Md = (double)M;
-  double sum = 0.0;
+    for (int j = 0; j < EPT; ++j) ml = fmaxf(ml, x[j]);
+    const uint32_t lk[1] = {has ? fkey(ml) : 0u};
+    const uint32_t tw = wave_kth_key<1, 32>(lk, k);
+    const float mw = wave_max_f32(ml);
+    const double md = (double)ml;
+    double sum = 0.0;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) sum += exp((double)x[j] - Md);
-  sum = wave_sum_f64(sum);
-  if (lane == 0) s_sum[wave] = sum;
-  __syncthreads();
-
-  if (wave == 0) {
-    // the chunk's top-k from the wave lists: lane l holds candidate l % k of wave l / k
-    const int nc = kChunkWaves * k;
-    float cv = lane < nc ? s_wv[lane / k][lane % k] : -INFINITY;
-    int ci = lane < nc ? s_wi[lane / k][lane % k] : INT32_MAX;
-    for (int t = 0; t < k; ++t) {
-      const int win = wave_argbest(ci != INT32_MAX ? fkey(cv) : 0u, ci);
-      if (win < 0) {
-        if (lane == 0) {
-          rec->val[t] = -INFINITY;
-          rec->id[t] = INT32_MAX;
-        }
-        continue;
-      }
-      if (lane == win) {
-        rec->val[t] = cv;
-        rec->id[t] = ci;
-        cv = -INFINITY;
-        ci = INT32_MAX;
-      }
+    for (int j = 0; j < EPT; ++j) {
+      const double e = exp_nonpos((double)x[j] - md, tab);
+      sum += in(j) ? e : 0.0;
     }
+    // the sum is complete here: otherwise the compiler sinks the exps past the barrier
+    // below, and every element's partial results stay live across it
+    asm volatile("" : "+v"(sum));
+    // a NaN or infinite logit makes its lane's sum NaN (and only that does)
+    const bool wbad = __ballot(sum != sum) != 0ull;
     if (lane == 0) {
+      s_thr[wave] = tw;
+      s_max[wave] = mw;
+      s_bad[wave] = wbad;
+    }
+    __syncthreads();
+    uint32_t T = s_thr[0];
+    float M = s_max[0];
+    int anybad = s_bad[0];
+#pragma unroll
+    for (int w = 1; w < kChunkWaves; ++w) {
+      T = max(T, s_thr[w]);
+      M = fmaxf(M, s_max[w]);
+      anybad |= s_bad[w];
+    }
+    if (anybad) {
+      if (tid == 0) rec->bad = 1;
+      return;
+    }
+    // the candidates: logits >= T (every logit of the chunk when T is 0)
+    const float tf = T == 0u ? -INFINITY : key_value(T);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const bool cj = in(j) && x[j] >= tf;
+      const uint64_t bm = __ballot(cj);
+      if (bm != 0ull) {
+        if (cj) {
+          const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (pos < kCandW) {
+            s_cv[wave][pos] = x[j];
+            s_ci[wave][pos] = id_of(j);
+          }
+        }
+        cnt += __popcll(bm);
+      }
+    }
+    // this lane's sum rescaled to the chunk maximum (lanes without logits hold 0)
+    sum *= exp_nonpos(md - (double)M, tab);
+    sum = wave_sum_f64_dpp(sum);
+    if (lane == 0) {
+      s_cnt[wave] = cnt;
+      s_sum[wave] = sum;
+    }
+    __syncthreads();
+    int n[kChunkWaves];
+    int total = 0;
+    bool over = false;
+#pragma unroll
+    for (int w = 0; w < kChunkWaves; ++w) {
+      n[w] = s_cnt[w];
+      total += n[w];
+      over |= n[w] > kCandW;
+    }
+    if (tid == 0) {
       double S = 0.0;
+#pragma unroll
       for (int w = 0; w < kChunkWaves; ++w) S += s_sum[w];
       rec->sum = S;
       rec->max = M;
       rec->bad = 0;
     }
+    if (!over && total <= kWave) {
+      // one wave ranks them (value descending, then id ascending): candidate `lane` in
+      // registers, the others read across lanes
+      if (wave == 0) {
+        int w0 = 0, i0 = lane;
+#pragma unroll
+        for (int w = 0; w < kChunkWaves - 1; ++w)
+          if (w0 == w && i0 >= n[w]) {
+            i0 -= n[w];
+            w0 = w + 1;
+          }
+        const bool mine = lane < total;
+        const float v = mine ? s_cv[w0][i0] : 0.f;
+        const int id = mine ? s_ci[w0][i0] : 0;
+        const uint64_t key = rank_key(v, id);
+        s_ck[lane] = key;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int rk = lds_rank_desc(s_ck, total, key);
+        if (mine && rk < k) {
+          rec->val[rk] = v;
+          rec->id[rk] = id;
+        }
+        if (lane >= total && lane < k) {                 // fewer logits than k
+          rec->val[lane] = -INFINITY;
+          rec->id[lane] = INT32_MAX;
+        }
+      }
+      return;
+    }
+    if (!over) {
+      // rank of candidate tid among all, by every thread
+      if (tid < total) {
+        int w0 = 0, i0 = tid;
+#pragma unroll
+        for (int w = 0; w < kChunkWaves - 1; ++w)
+          if (w0 == w && i0 >= n[w]) {
+            i0 -= n[w];
+            w0 = w + 1;
+          }
+        const float v = s_cv[w0][i0];
+        const int id = s_ci[w0][i0];
+        int rk = 0;
+        for (int w = 0; w < kChunkWaves; ++w)
+          for (int i = 0; i < n[w]; ++i) {
+            const float ov = s_cv[w][i];
+            const int oi = s_ci[w][i];
+            rk += (int)(ov > v) | ((int)(ov == v) & (int)(oi < id));
+          }
+        if (rk < k) {
+          rec->val[rk] = v;
+          rec->id[rk] = id;
+        }
+      }
+      if (tid >= total && tid < k) {                     // fewer logits than k
+        rec->val[tid] = -INFINITY;
+        rec->id[tid] = INT32_MAX;
+      }
+      return;
+    }
+
+    // Heavy ties: exact selection.  Each wave takes its top-k in k rounds over the
+    // lanes' heads (a lane keeps its best two; when it wins with its second already
+    // promoted, it rescans for the two after the winner); wave 0 then merges the lists.
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) x[j] = in(j) ? x[j] : -INFINITY;
+    }
+    float h1v, h2v;
+    int h1j, h2j;
+    best_two(x, INFINITY, -1, h1v, h1j, h2v, h2j);
+    bool second_known = true;
+    for (int t = 0; t < k; ++t) {
+      const int win = wave_argbest(h1j < EPT ? fkey(h1v) : 0u, id_of(h1j));
+      if (win < 0) {
+        if (lane == 0) {
+          s_wv[wave][t] = -INFINITY;
+          s_wi[wave][t] = INT32_MAX;
+        }
+        continue;
+      }
+      if (lane == win) {
+        s_wv[wave][t] = h1v;
+        s_wi[wave][t] = id_of(h1j);
+        if (second_known) {
+          h1v = h2v;
+          h1j = h2j;
+          second_known = false;
+        } else {
+          float a1v, a2v;
+          int a1j, a2j;
+          best_two(x, h1v, h1j, a1v, a1j, a2v, a2j);
+          h1v = a1v;
+          h1j = a1j;
+          h2v = a2v;
+          h2j = a2j;
+          second_known = true;
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds candidate l % k of wave l / k
+      const int nc = kChunkWaves * k;
+      float cv = lane < nc ? s_wv[lane / k][lane % k] : -INFINITY;
+      int ci = lane < nc ? s_wi[lane / k][lane % k] : INT32_MAX;
+      for (int t = 0; t < k; ++t) {
+        const int win = wave_argbest(ci != INT32_MAX ? fkey(cv) : 0u, ci);
+        if (win < 0) {
+          if (lane == 0) {
+            rec->val[t] = -INFINITY;
+            rec->id[t] = INT32_MAX;
+          }
+          continue;
+        }
+        if (lane == win) {
+          rec->val[t] = cv;
+          rec->id[t] = ci;
+          cv = -INFINITY;
+          ci = INT32_MAX;
+        }
+      }
+    }
+  };
+  if (e1 - e0 == EPT * kChunkThreads)
+    body(std::integral_constant<bool, false>());
+  else
+    body(std::integral_constant<bool, true>());
+}
+
+// wave-scope ordering of one wave's LDS writes before its reads of them
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The k best entries, by (value descending, id ascending), of up to 64 lists held one
+// per lane, each best first: lane l's list has len entries, value(j) and id(j) (ids
+// distinct, >= 0); at most max_total entries in all.  When they may exceed kWave and at
+// least k lists are non-empty, T = the k-th best list head bounds them: every entry at
+// or above it is a candidate, and at least k are.  Otherwise every entry is.  The
+// candidates' rank keys are compacted into buf (kWave + 1 entries of this wave's LDS)
+// and ranked there; emit(rank, key) is called for ranks below k.  Returns false,
+// emitting nothing, when there are more than kWave candidates (heavy ties): the caller
+// then merges another way.  Every lane must call.
+template <class Val, class Id, class Emit>
+__device__ __forceinline__ bool wave_topk_of_lists(int len, Val value, Id id_at, int k,
+                                                  int max_total, uint64_t* buf, Emit emit) {
+  const int lane = lane_id();
+  uint64_t T = 0;
+  if (max_total > kWave && __popcll(__ballot(len > 0)) >= k) {
+    const uint64_t hk = len > 0 ? rank_key(value(0), id_at(0)) : 0ull;
+    buf[lane] = hk;
+    wave_lds_sync();
+    if (len > 0 && lds_rank_desc(buf, kWave, hk) == k - 1) buf[kWave] = hk;
+    wave_lds_sync();
+    T = buf[kWave];
+    wave_lds_sync();
   }
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kTopKMax; ++j) cnt += (int)(j < len && rank_key(value(j), id_at(j)) >= T);
+  // this lane's candidates go to buf[first ..], first = the counts of the lanes below
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    incl += lane >= o ? t : 0;
+  }
+  const int n = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (n > kWave) return false;
+  const int first = incl - cnt;
+#pragma unroll
+  for (int j = 0; j < kTopKMax; ++j)
+    if (j < cnt) buf[first + j] = rank_key(value(j), id_at(j));
+  wave_lds_sync();
+  if (lane < n) {
+    const uint64_t key = buf[lane];
+    const int rk = lds_rank_desc(buf, n, key);
+    if (rk < k) emit(rk, key);
+  }
+  return true;
 }
 
 __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
@@ -329,7 +598,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   PoolEntry* pool = (PoolEntry*)(seq + sizeof(SeqHeader));
   const ChunkRec* recs = (const ChunkRec*)(seq + rec_off);
 
-  __shared__ __align__(16) float s_score[kTopKMax * kTopKMax];   // read as float4 when ranking
+  __shared__ float s_score[kTopKMax * kTopKMax];
   __shared__ uint32_t s_key[kPoolMax];
   __shared__ uint8_t s_dep[kPoolMax];
   __shared__ short s_pos[kPoolMax];
@@ -349,6 +618,8 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   __shared__ int s_status;
   __shared__ int s_m;
   __shared__ int s_rowbad;
+  __shared__ uint64_t s_mk[kSelWaves][kWave + 1];    // per-wave merge candidates
+  __shared__ uint64_t s_ckey[kTopKMax * kTopKMax];    // this level's children, rank keys
 
   const int base = pool_base(k, step);
   const int added = rows * k;
@@ -368,8 +639,6 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     s_rowbad = 0;
   }
   if (tid < kTopKMax) s_front[tid] = -1;
-  const int added16 = (added + 15) & ~15;
-  if (tid >= added && tid < added16) s_score[tid] = -INFINITY;   // ranks after every child
   const int rr = wave;
   const bool merger = rr < rows;
   const bool has = merger && lane < nch;
@@ -384,15 +653,35 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
   int pdepth = 0;
   if (merger) {
     // records of a sequence that is not ok are stale but never used
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) {
+      hv[j] = -INFINITY;
+      hi[j] = INT32_MAX;
+    }
     if (has) {
       cbad = rec->bad;
       cmax = rec->max;
       csum = rec->sum;
-    }
+      // whole 16-byte pieces (a record is 144 bytes, its lists 16-byte aligned), then the
+      // places past k are cleared
 #pragma unroll
-    for (int j = 0; j < kTopKMax; ++j) {
-      hv[j] = has && j < k ? rec->val[j] : -INFINITY;
-      hi[j] = has && j < k ? rec->id[j] : INT32_MAX;
+      for (int q = 0; q < kTopKMax / 4; ++q) {
+        const float4 v4 = ((const float4*)rec->val)[q];
+        const int4 i4 = ((const int4*)rec->id)[q];
+        hv[4 * q] = v4.x;
+        hv[4 * q + 1] = v4.y;
+        hv[4 * q + 2] = v4.z;
+        hv[4 * q + 3] = v4.w;
+        hi[4 * q] = i4.x;
+        hi[4 * q + 1] = i4.y;
+        hi[4 * q + 2] = i4.z;
+        hi[4 * q + 3] = i4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < kTopKMax; ++j) {
+        hv[j] = j < k ? hv[j] : -INFINITY;
+        hi[j] = j < k ? hi[j] : INT32_MAX;
+      }
     }
     if (step > 1) {
       // the frontier holds the previous level's children: depth step - 1
@@ -412,20 +701,32 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
       if (lane == 0) s_rowbad = 1;
     } else {
       const float M = wave_max_f32(cmax);
-      const double S = wave_sum_f64(has ? csum * exp((double)cmax - (double)M) : 0.0);
+      const double S = wave_sum_f64_dpp(has ? csum * exp((double)cmax - (double)M) : 0.0);
       const float lse32 = (float)((double)M + log(S));
-      for (int t = 0; t < k; ++t) {
+      // a chunk's list holds its valid entries first (-inf / INT32_MAX past them)
+      int len = 0;
+#pragma unroll
+      for (int j = 0; j < kTopKMax; ++j) len += (int)(hi[j] != INT32_MAX);
+      auto put_child = [&](int t, float v, int tok) {
+        PoolEntry e;
+        e.parent_slot = pslot;
+        e.token = tok;
+        e.score = __fadd_rn(pscore, __fsub_rn(v, lse32));
+        e.depth = pdepth + 1;
+        pool[base + rr * k + t] = e;
+        s_score[rr * k + t] = e.score;
+        s_tok[rr * k + t] = e.token;
+        s_ckey[rr * k + t] = rank_key(e.score, rr * k + t);
+      };
+      const bool merged = wave_topk_of_lists(
+          len, [&](int j) { return hv[j]; }, [&](int j) { return hi[j]; }, k, nch * k, s_mk[rr],
+          [&](int t, uint64_t key) { put_child(t, key_float(key), key_id(key)); });
+      // heavy ties: k rounds of the best head
+      for (int t = 0; !merged && t < k; ++t) {
         // the chunks together hold at least k finite candidates (vocab >= k)
         const int win = wave_argbest(hi[0] != INT32_MAX ? fkey(hv[0]) : 0u, hi[0]);
         if (lane == win) {
-          PoolEntry e;
-          e.parent_slot = pslot;
-          e.token = hi[0];
-          e.score = __fadd_rn(pscore, __fsub_rn(hv[0], lse32));
-          e.depth = pdepth + 1;
-          pool[base + rr * k + t] = e;
-          s_score[rr * k + t] = e.score;
-          s_tok[rr * k + t] = e.token;
+          put_child(t, hv[0], hi[0]);
 #pragma unroll
           for (int j = 0; j < kTopKMax - 1; ++j) {
             hv[j] = hv[j + 1];
@@ -438,30 +739,17 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int st = s_status;
-    if (st == TV_SEQ_OK && s_rowbad) st = TV_SEQ_NONFINITE;
-    if (st == TV_SEQ_OK && final_m > 0 && (s_m < 1 || s_m > n_max)) st = TV_SEQ_BAD_N;
-    s_status = st;
-  }
-  __syncthreads();
-  const int st = s_status;
+  // every thread derives the status from the same LDS words
+  int st = s_status;
+  if (st == TV_SEQ_OK && s_rowbad) st = TV_SEQ_NONFINITE;
+  if (st == TV_SEQ_OK && final_m > 0 && (s_m < 1 || s_m > n_max)) st = TV_SEQ_BAD_N;
 
   if (st == TV_SEQ_OK) {
-    // next frontier: the k best children of this level by (score desc, creation asc)
+    // next frontier: the k best children of this level by (score desc, creation asc):
+    // each child's rank among all of them, from their rank keys in LDS
     for (int c = tid; c < added; c += kSelThreads) {
-      const float sc = s_score[c];
-      int rank = 0;
-      for (int o = 0; o < added16; o += 16) {
-        float4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = *(const float4*)&s_score[o + 4 * j];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          rank += beats(v[j].x, o + 4 * j, sc, c) + beats(v[j].y, o + 4 * j + 1, sc, c) +
-                  beats(v[j].z, o + 4 * j + 2, sc, c) + beats(v[j].w, o + 4 * j + 3, sc, c);
-      }
-      if (rank < k) s_front[rank] = c;
+      const int rk = lds_rank_desc(s_ckey, added, s_ckey[c]);
+      if (rk < k) s_front[rk] = c;
     }
     __syncthreads();
     if (tid < k) {
@@ -694,8 +982,8 @@ __global__ __launch_bounds__(kSelThreads) void draft_continue_kernel(
   if (tid == 0) more[b] = s_fail ? 0 : 1;
 }
 
-// Chunking of a logit row: about 1024 workgroups in all, each chunk between 1024 and
-// 8192 logits where the vocabulary allows, at most kMaxRowChunks chunks per row.
+// Chunking of a logit row: about 1024 workgroups in all, each chunk 2048, 4096, 8192 or
+// 16384 logits (8 to 64 per thread), at most kMaxRowChunks chunks per row.
 struct RowPlan {
   int nch, chunk, ept;
 };
@@ -709,12 +997,12 @@ static RowPlan row_plan(int B, int rows, int vocab) {
   if (n < lo) n = lo;
   if (n > kMaxRowChunks) n = kMaxRowChunks;
   if (n < 1) n = 1;
-  int ch = (int)((vocab + n - 1) / n);
-  ch = (ch + 3) & ~3;
+  const int ch = (int)((vocab + n - 1) / n);
   RowPlan p;
-  p.chunk = ch;
-  p.nch = (vocab + ch - 1) / ch;
   p.ept = ch <= 8 * kChunkThreads ? 8 : ch <= 16 * kChunkThreads ? 16 : ch <= 32 * kChunkThreads ? 32 : 64;
+  // whole chunks of EPT logits per thread: only a row's last chunk takes bounds tests
+  p.chunk = p.ept * kChunkThreads;
+  p.nch = (vocab + p.chunk - 1) / p.chunk;
   return p;
 }
 
