@@ -176,7 +176,8 @@ tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int
  * Each dot product is a float64 sum of the exact products, rounded once to float32.
  * The rows feed tree_expand_rerank unchanged (their log-sum-exp, top-k and scores).
  * Outputs: logits fp32 [rows][vocab], cand int32 [rows][C].  All device pointers,
- * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r) bytes (z), no
+ * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r) bytes (z in float64,
+ * rows padded to whole groups of 16), no
  * initialisation needed.
  * Limits: d % 8 == 0, r % 32 == 0, 32 <= r <= 512, 1 <= C <= 256, C <= vocab.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED (alignment), TV_ERR_WORKSPACE.

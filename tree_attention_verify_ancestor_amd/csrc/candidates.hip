@@ -13,17 +13,24 @@
 // output bit are fixed up to the order of a float64 sum.
 //
 // Four kernels per call:
-//   cand_z_kernel      one wave per (row, j): z[row][j], lanes split d, float64 sums
-//   cand_score_kernel  four lanes per token (each a quarter of r), two tokens per
-//                      thread, rows in groups of 8
-//                      with z in LDS: the low-rank scores, written into the logits rows
-//   cand_select_kernel one workgroup per row: a lower bound on the C-th best score from
-//                      the threads' maxima, the few scores above it gathered in LDS and
-//                      ranked there (ties to the lower id); with heavy ties, radix
-//                      selection over the whole row on order-preserving keys
+//   cand_z_kernel      one wave per (row, j): z[row][j], lanes split d, float64 sums;
+//                      stored as float64 (the float32 value upcast) at [group][j][16],
+//                      rows padded to whole groups of 16 with zeros
+//   cand_score_kernel  64 tokens per workgroup: their Bm rows are read once, coalesced,
+//                      into LDS; each of 4 waves takes a quarter of the group's rows, a
+//                      lane one token, and sums over j in float64 with z read as scalars
+//                      (the same for every lane): the low-rank scores, written into the
+//                      logits rows.  At 10 rows this is about 10 flops per Bm byte, the
+//                      float64 ridge of the vector ALUs, so exact sums cost about the
+//                      HBM time.
+//   cand_select_kernel one workgroup per row: the C-th largest of 256 group maxima
+//                      (groups of four threads' strided tokens) bounds the C-th best
+//                      score from below; the few scores at or above it are gathered in
+//                      LDS and ranked there (ties to the lower id); with heavy ties,
+//                      radix selection over the whole row on order-preserving keys
 //   cand_exact_kernel  one wave per (row, candidate): its exact logit overwrites the
 //                      score
-// HBM traffic: Bm (V*r*2 B) once per group of 8 rows, the C rows of W per draft row
+// HBM traffic: Bm (V*r*2 B) once per group of 16 rows, the C rows of W per draft row
 // (C*d*2 B), A once per row, and the logits rows written then read once.
 #include "tv_internal.h"
 
@@ -31,12 +38,11 @@ namespace tv {
 
 constexpr int kCandMaxC = 256;
 constexpr int kCandMaxR = 512;
-constexpr int kCandGroup = 8;                  // rows per score workgroup
-constexpr int kCandSplit = 4;                  // lanes per token in the score kernel
-constexpr int kScoreBatch = 8;                 // Bm loads in flight per score thread
+constexpr int kCandGroup = 16;                 // rows per score pass (z padded to whole groups)
+constexpr int kScoreWaves = 4;                 // waves per score workgroup
 constexpr int kCandSelThreads = 1024;
 constexpr int kCandGather = 2048;              // keys above the lower bound ranked in LDS
-constexpr int kCandCache = 32 * 1024;          // vocabularies whose keys stay in LDS
+constexpr int kCandGroups = kCandSelThreads / 4;   // groups of four threads for the lower bound
 
 // Order-preserving map of a float to an unsigned key: a larger value has a larger key,
 // -0 and +0 share one key.
@@ -76,83 +82,144 @@ __device__ __forceinline__ double wave_dot_bf16(const __bf16* a, const __bf16* b
   return wave_sum_d(acc);
 }
 
-__global__ __launch_bounds__(256) void cand_z_kernel(int d, int r, const __bf16* __restrict__ h,
-                                                    const __bf16* __restrict__ A, float* __restrict__ z) {
+// z[row][j] rounded once to float32, stored upcast at z64[(row/16 * r + j) * 16 + row%16];
+// rows past the last one (up to the group's end) hold 0
+__global__ __launch_bounds__(256) void cand_z_kernel(int rows, int d, int r, const __bf16* __restrict__ h,
+                                                    const __bf16* __restrict__ A, double* __restrict__ z64) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int j = blockIdx.x * 4 + wave;
   const int row = blockIdx.y;
   if (j >= r) return;                                          // wave-uniform
-  const double s = wave_dot_bf16(h + (size_t)row * d, A + (size_t)j * d, d, lane);
-  if (lane == 0) z[(size_t)row * r + j] = (float)s;
+  const double s = row < rows ? wave_dot_bf16(h + (size_t)row * d, A + (size_t)j * d, d, lane) : 0.0;
+  if (lane == 0)
+    z64[((size_t)(row / kCandGroup) * r + j) * kCandGroup + row % kCandGroup] = (double)(float)s;
 }
 
-// TPT tokens per thread (token u at v0 + u * 64): each z value is read from LDS and
-// converted to float64 once for TPT products.  Every token's sum keeps the order of
-// one token per thread: j increasing, then the four quarters combined.
-template <int TPT>
-__global__ __launch_bounds__(256) void cand_score_kernel(int rows, int r, int V,
-                                                        const __bf16* __restrict__ Bm,
-                                                        const float* __restrict__ z,
-                                                        float* __restrict__ logits) {
-  constexpr int kTok = 256 / kCandSplit;
-  __shared__ float sz[kCandGroup * kCandMaxR];
-  const int g0 = blockIdx.y * kCandGroup;
-  const int gr = min(kCandGroup, rows - g0);
-  for (int t = threadIdx.x; t < gr * r; t += blockDim.x) sz[t] = z[(size_t)g0 * r + t];
+// Eight lanes share a token row: lane (t, p), t = lane / 8, p = lane % 8, takes the
+// 8-j chunks p, p + 8, p + 16, ... of the rows of its TPT tokens t0 + t + 8u (u < TPT),
+// so the eight lanes' 16-byte loads of one chunk index cover a whole 128-byte line of a
+// row.  ROWS (even) rows of the group, z zero past the last row; z comes from LDS, one
+// 16-byte read giving two rows of one j, shared by the TPT tokens.  Each token's sum: a
+// lane's j in increasing order, then the eight lanes combined by neighbours, pairs, then
+// halves -- one fixed order.
+template <int ROWS, int TPT, int RMAX>
+__global__ __launch_bounds__(kScoreWaves * kWave) void cand_score_kernel(
+    int rows, int r, int V, const __bf16* __restrict__ Bm, const double* __restrict__ z64,
+    float* __restrict__ logits) {
+  static_assert(ROWS % 2 == 0 && ROWS <= kCandGroup, "rows in pairs, at most one group");
+  constexpr int kQMax = (RMAX + 63) / 64;             // chunks per lane at most
+  // lane part p's z: zs[p * kPart + (q * 8 + e) * ROWS + row] = z[row][(8q + p) * 8 + e];
+  // each part padded by 16 bytes, so the eight parts of one read fall on distinct banks
+  constexpr int kPart = kQMax * 8 * ROWS + 2;
+  __shared__ __align__(16) double zs[8 * kPart];
+  constexpr int kTokW = 8 * TPT;                      // tokens per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int g = blockIdx.y;
+  const int nch = r / 8;                              // 8-j chunks of a row
+  const int nq = (nch + 7) / 8;                       // chunks per lane (the last may be partial)
+  // the group's z: every load of a batch issued before any store
+  const double* zg = z64 + (size_t)g * r * kCandGroup;
+  constexpr int kThr = kScoreWaves * kWave;
+  constexpr int kBatch = 16;
+  const int nz = r * ROWS;
+  for (int q0 = 0; q0 < nz; q0 += kBatch * kThr) {
+    double zv[kBatch];
+#pragma unroll
+    for (int bt = 0; bt < kBatch; ++bt) {
+      const int qq = min(q0 + bt * kThr + tid, nz - 1);
+      zv[bt] = zg[(qq / ROWS) * kCandGroup + qq % ROWS];
+    }
+#pragma unroll
+    for (int bt = 0; bt < kBatch; ++bt) {
+      const int qq = q0 + bt * kThr + tid;
+      if (qq < nz) {
+        const int j = qq / ROWS, row = qq % ROWS, c = j / 8;
+        zs[(c % 8) * kPart + ((c / 8) * 8 + j % 8) * ROWS + row] = zv[bt];
+      }
+    }
+  }
+  // chunks past the row (the last round when r is not a multiple of 64) read z as 0:
+  // their Bm pieces are zeros, and 0 * z must not meet an unwritten (possibly NaN) word
+  const int n_pad = (nq * 8 - nch) * 8 * ROWS;
+  for (int qq = tid; qq < n_pad; qq += kThr) {
+    const int c = nch + qq / (8 * ROWS), rest = qq % (8 * ROWS);
+    zs[(c % 8) * kPart + (c / 8) * 8 * ROWS + rest] = 0.0;
+  }
   __syncthreads();
-  const int v0 = blockIdx.x * kTok * TPT + threadIdx.x / kCandSplit;
-  const int part = threadIdx.x % kCandSplit;
-  const int rq = r / kCandSplit;
-  double acc[TPT][kCandGroup];
+  const int t = lane >> 3, p = lane & 7;
+  const int tw0 = (blockIdx.x * kScoreWaves + wave) * kTokW;
+  const __bf16* brow[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) brow[u] = Bm + (size_t)min(tw0 + t + 8 * u, V - 1) * r;
+  const double* zp = zs + p * kPart;
+  double acc[TPT][ROWS];
 #pragma unroll
   for (int u = 0; u < TPT; ++u)
 #pragma unroll
-    for (int k = 0; k < kCandGroup; ++k) acc[u][k] = 0.0;
-  const float* zp = sz + part * rq;
-  for (int jb = 0; jb < rq; jb += 8 * kScoreBatch) {
-    bf16x8 bv[TPT][kScoreBatch];
+    for (int i = 0; i < ROWS; ++i) acc[u][i] = 0.0;
+  // blocks of 4 chunks per lane: every 16-byte piece of the block, for each token, is
+  // loaded before any is used (all of a lane's chunks when r <= 256); a chunk past the
+  // row reads as zeros, which add nothing
+  constexpr int kQB = 4;
+  for (int qb = 0; qb < nq; qb += kQB) {
+    uint4 piece[kQB][TPT];
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const __bf16* bp = Bm + (size_t)min(v0 + u * kTok, V - 1) * r + part * rq;
+    for (int q = 0; q < kQB; ++q) {
+      const int c = (qb + q) * 8 + p;
 #pragma unroll
-      for (int q = 0; q < kScoreBatch; ++q) bv[u][q] = *(const bf16x8*)(bp + min(jb + 8 * q, rq - 8));
+      for (int u = 0; u < TPT; ++u) {
+        piece[q][u] = *(const uint4*)(brow[u] + 8 * min(c, nch - 1));
+        if (c >= nch) piece[q][u] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < kScoreBatch; ++q) {
-      const int j0 = jb + 8 * q;
-      if (j0 < rq) {
+    for (int q = 0; q < kQB; ++q) {
+      if (qb + q >= nq) break;
 #pragma unroll
-        for (int k = 0; k < kCandGroup; ++k) {
-          if (k < gr) {
+      for (int e = 0; e < 8; ++e) {
+        const double2* zj = (const double2*)(zp + ((qb + q) * 8 + e) * ROWS);
+        double bd[TPT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const double zv = (double)zp[k * r + j0 + e];
+        for (int u = 0; u < TPT; ++u) {
+          const uint32_t w32 = e < 2 ? piece[q][u].x : e < 4 ? piece[q][u].y : e < 6 ? piece[q][u].z : piece[q][u].w;
+          bd[u] = (double)__uint_as_float((e & 1) ? (w32 & 0xFFFF0000u) : (w32 << 16));
+        }
 #pragma unroll
-              for (int u = 0; u < TPT; ++u)
-                acc[u][k] = fma((double)(float)bv[u][q][e], zv, acc[u][k]);
-            }
+        for (int i2 = 0; i2 < ROWS / 2; ++i2) {
+          const double2 zz = zj[i2];
+#pragma unroll
+          for (int u = 0; u < TPT; ++u) {
+            acc[u][2 * i2] = fma(bd[u], zz.x, acc[u][2 * i2]);
+            acc[u][2 * i2 + 1] = fma(bd[u], zz.y, acc[u][2 * i2 + 1]);
           }
         }
       }
     }
   }
+  // the eight lanes of each token, by DPP within each group of eight: pairs (quad_perm
+  // [1,0,3,2]), quads ([2,3,0,1]), then the two quads (half-row mirror); every lane of
+  // a group ends with the same sum
 #pragma unroll
   for (int u = 0; u < TPT; ++u)
 #pragma unroll
-    for (int k = 0; k < kCandGroup; ++k) {
-      acc[u][k] += __shfl_xor(acc[u][k], 1);
-      acc[u][k] += __shfl_xor(acc[u][k], 2);
+    for (int i = 0; i < ROWS; ++i) {
+      double a = acc[u][i];
+      a += dpp_f64<0xB1>(a);
+      a += dpp_f64<0x4E>(a);
+      a += dpp_f64<0x141>(a);
+      acc[u][i] = a;
     }
-  if (part == 0) {
+  // lane p of each group writes rows p, p + 8 of its tokens
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int v = v0 + u * kTok;
-      if (v < V) {
+  for (int u = 0; u < TPT; ++u) {
+    const int v = tw0 + t + 8 * u;
 #pragma unroll
-        for (int k = 0; k < kCandGroup; ++k)
-          if (k < gr) logits[(size_t)(g0 + k) * V + v] = (float)acc[u][k];
-      }
+    for (int i = 0; i < ROWS; ++i) {
+      const int row = g * kCandGroup + i;
+      if ((i & 7) == p && row < rows && v < V) logits[(size_t)row * V + v] = (float)acc[u][i];
     }
   }
 }
@@ -165,14 +232,12 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   const int wave = tid / kWave;
   const float* lrow = logits + (size_t)row * V;
   __shared__ uint32_t s_hist[256];
-  __shared__ int s_digit, s_before, s_n, s_ties, s_cnt;
-  __shared__ uint32_t s_tmax[kCandSelThreads];
-  __shared__ uint32_t s_gk[kCandGather];
-  __shared__ int s_gi[kCandGather];
+  __shared__ int s_digit, s_before, s_n, s_ties;
+  __shared__ uint32_t s_gmax[kCandGroups];
+  __shared__ uint64_t s_gk[kCandGather];
   __shared__ int s_ids[kCandMaxC];
   __shared__ uint32_t s_keys[kCandMaxC];
   __shared__ int s_rank[kCandMaxC];
-  __shared__ uint32_t s_row[kCandCache];
 
   // every pass over the row: 32 coalesced key loads per thread in flight, then the
   // body for each (id, key)
@@ -199,11 +264,13 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   };
   // Radix selection, 8 bits at a time from the top, over the keys each_key visits:
   // T = the k-th largest key; `need` = how many entries equal to T complete the k.
-  auto radix_select = [&](auto&& each_key, int k, uint32_t& T, int& need) {
+  // With passes < 4, T is the k-th largest key's leading 8 * passes bits (the rest 0):
+  // a lower bound with at least k keys at or above it.
+  auto radix_select = [&](auto&& each_key, int k, uint32_t& T, int& need, int passes) {
     uint32_t tmask = 0;
     T = 0;
     need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= 32 - 8 * passes; shift -= 8) {
       if (tid < 256) s_hist[tid] = 0u;
       __syncthreads();
       each_key([&](int, uint32_t u) {
@@ -247,55 +314,77 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
     }
   };
 
-  // the row's keys stay in LDS when they fit: one pass over global memory, the others
-  // over LDS
-  const bool cached = V <= kCandCache;
-  auto each_key = [&](auto&& body) {
-    if (cached) {
-      for (int v = tid; v < V; v += kCandSelThreads) body(v, s_row[v]);
-    } else {
-      for_each_key(body);
-    }
-  };
-
-  // A lower bound first: each thread's largest key, and T0 the C-th largest of those
-  // (C threads hold a key >= T0, so the C best keys are all >= T0).  The keys >= T0
-  // are usually few: they are gathered in LDS and ranked there.
+  // A lower bound first: the largest key of each group of four threads (their strided
+  // tokens), and T0 the C-th largest of those 256 group maxima: C groups hold a key
+  // >= T0, so the C best keys are all >= T0.  The keys >= T0 are usually few (C plus a
+  // few dozen): they are gathered in LDS and ranked there.  A row of at most
+  // kBatch * 1024 tokens is read once and its keys stay in registers.
+  const bool one_pass = V <= kBatch * kCandSelThreads;
+  uint32_t u1[kBatch];
   uint32_t tmax = 0;
-  for_each_key([&](int v, uint32_t u) {
-    tmax = max(tmax, u);
-    if (cached) s_row[v] = u;
-  });
-  s_tmax[tid] = tmax;
-  if (tid == 0) s_cnt = 0;
+  if (one_pass) {
+    float x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) x[j] = lrow[min(j * kCandSelThreads + tid, V - 1)];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      u1[j] = j * kCandSelThreads + tid < V ? cand_key(x[j]) : 0u;
+      tmax = max(tmax, u1[j]);
+    }
+  } else {
+    for_each_key([&](int, uint32_t u) { tmax = max(tmax, u); });
+  }
+  tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0xB1, 0xF, 0xF, false));
+  tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0x4E, 0xF, 0xF, false));
+  if ((tid & 3) == 0) s_gmax[tid >> 2] = tmax;
+  if (tid == 0) s_n = 0;
   __syncthreads();
+  // T0: the leading 16 bits of the C-th largest group maximum (C <= 256 groups), by two
+  // radix passes; at least C group maxima, hence C keys, are >= T0
   uint32_t T0;
   int need0;
-  radix_select([&](auto&& body) { body(tid, s_tmax[tid]); }, C, T0, need0);
-  int ge = 0;
-  each_key([&](int, uint32_t u) { ge += u >= T0; });
-  if (ge) atomicAdd(&s_cnt, ge);
-  __syncthreads();
-  const int n_ge = s_cnt;
-  if (n_ge <= kCandGather) {
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    each_key([&](int v, uint32_t u) {
+  radix_select([&](auto&& body) { if (tid < kCandGroups) body(tid, s_gmax[tid]); }, C, T0, need0, 2);
+  // gather the keys >= T0: per-thread counts, a wave prefix sum, one atomic per wave
+  int mine = 0;
+  if (one_pass) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mine += (int)(u1[j] >= T0 && j * kCandSelThreads + tid < V);
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int tt = __shfl_up(incl, o);
+      incl += lane >= o ? tt : 0;
+    }
+    int wbase = 0;
+    if (lane == kWave - 1) wbase = atomicAdd(&s_n, incl);
+    wbase = __shfl(wbase, kWave - 1);
+    int slot = wbase + incl - mine;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int v = j * kCandSelThreads + tid;
+      if (u1[j] >= T0 && v < V) {
+        if (slot < kCandGather) s_gk[slot] = ((uint64_t)u1[j] << 32) | (uint32_t)~v;
+        ++slot;
+      }
+    }
+  } else {
+    for_each_key([&](int v, uint32_t u) {
       if (u >= T0) {
         const int slot = atomicAdd(&s_n, 1);
-        s_gk[slot] = u;
-        s_gi[slot] = v;
+        if (slot < kCandGather) s_gk[slot] = ((uint64_t)u << 32) | (uint32_t)~v;
       }
     });
-    __syncthreads();
-    // rank by (larger key, lower id); the first C are the candidates
+  }
+  __syncthreads();
+  const int n_ge = s_n;
+  if (n_ge <= kCandGather) {
+    // rank by (larger key, lower id) from the packed keys; the first C are the candidates
     for (int gi = tid; gi < n_ge; gi += kCandSelThreads) {
-      const uint32_t km = s_gk[gi];
-      const int im = s_gi[gi];
+      const uint64_t km = s_gk[gi];
       int rk = 0;
-      for (int o = 0; o < n_ge; ++o)                 // branch-free: no exec-mask jumps
-        rk += (int)(s_gk[o] > km) | ((int)(s_gk[o] == km) & (int)(s_gi[o] < im));
-      if (rk < C) s_rank[rk] = im;
+#pragma unroll 8
+      for (int o = 0; o < n_ge; ++o) rk += (int)(s_gk[o] > km);
+      if (rk < C) s_rank[rk] = (int)~(uint32_t)km;
     }
     __syncthreads();
     if (tid < C) cand[(size_t)row * C + tid] = s_rank[tid];
@@ -308,7 +397,7 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   // order.
   uint32_t T;
   int need;
-  radix_select(for_each_key, C, T, need);
+  radix_select(for_each_key, C, T, need, 4);
   if (tid == 0) {
     s_n = 0;
     s_ties = 0;
@@ -375,8 +464,37 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(int d, int V, int C,
 
 TV_API size_t tree_candidate_workspace_size(int rows, int r) {
   if (rows < 1 || r < 1 || r > tv::kCandMaxR) return 0;
-  return ((size_t)rows * r * sizeof(float) + 255) / 256 * 256;
+  const size_t groups = ((size_t)rows + tv::kCandGroup - 1) / tv::kCandGroup;
+  return (groups * tv::kCandGroup * r * sizeof(double) + 255) / 256 * 256;
 }
+
+namespace tv {
+template <int ROWS, int RMAX>
+static void launch_score_rows(int rows, int r, int vocab, const __bf16* Bm, const double* z64,
+                              float* logits, hipStream_t stream) {
+  constexpr int TPT = ROWS <= 12 ? 4 : 2;             // tokens per lane: acc stays <= 48 doubles
+  const int per_wg = kScoreWaves * 8 * TPT;
+  const dim3 grid((vocab + per_wg - 1) / per_wg, (rows + kCandGroup - 1) / kCandGroup);
+  hipLaunchKernelGGL((cand_score_kernel<ROWS, TPT, RMAX>), grid, dim3(kScoreWaves * kWave), 0, stream,
+                     rows, r, vocab, Bm, z64, logits);
+}
+template <int RMAX>
+static void launch_score(int rows, int r, int vocab, const __bf16* Bm, const double* z64,
+                         float* logits, hipStream_t stream) {
+  // the group's rows rounded up to even (whole groups of 16 past 16 rows)
+  const int rg = rows > kCandGroup ? kCandGroup : (rows + 1) & ~1;
+  switch (rg) {
+    case 2: launch_score_rows<2, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 4: launch_score_rows<4, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 6: launch_score_rows<6, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 8: launch_score_rows<8, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 10: launch_score_rows<10, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 12: launch_score_rows<12, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 14: launch_score_rows<14, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    default: launch_score_rows<16, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+  }
+}
+}  // namespace tv
 
 TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C, const void* h,
                                        const void* A, const void* Bm, const void* W,
@@ -390,14 +508,14 @@ TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C,
     return TV_ERR_UNSUPPORTED;
   const size_t need = tree_candidate_workspace_size(rows, r);
   if (!ws || ws_bytes < need) return TV_ERR_WORKSPACE;
-  float* z = (float*)ws;
-  hipLaunchKernelGGL(tv::cand_z_kernel, dim3((r + 3) / 4, rows), dim3(256), 0, stream, d, r,
-                     (const __bf16*)h, (const __bf16*)A, z);
-  constexpr int kTokensPerWg = 256 / tv::kCandSplit * 2;
-  hipLaunchKernelGGL(tv::cand_score_kernel<2>,
-                     dim3((vocab + kTokensPerWg - 1) / kTokensPerWg,
-                          (rows + tv::kCandGroup - 1) / tv::kCandGroup),
-                     dim3(256), 0, stream, rows, r, vocab, (const __bf16*)Bm, (const float*)z, logits);
+  double* z64 = (double*)ws;
+  const int padded = (rows + tv::kCandGroup - 1) / tv::kCandGroup * tv::kCandGroup;
+  hipLaunchKernelGGL(tv::cand_z_kernel, dim3((r + 3) / 4, padded), dim3(256), 0, stream, rows, d, r,
+                     (const __bf16*)h, (const __bf16*)A, z64);
+  if (r <= 256)
+    tv::launch_score<256>(rows, r, vocab, (const __bf16*)Bm, z64, logits, stream);
+  else
+    tv::launch_score<512>(rows, r, vocab, (const __bf16*)Bm, z64, logits, stream);
   hipLaunchKernelGGL(tv::cand_select_kernel, dim3(rows), dim3(tv::kCandSelThreads), 0, stream,
                      vocab, C, (const float*)logits, cand);
   hipLaunchKernelGGL(tv::cand_exact_kernel, dim3((C + 3) / 4, rows), dim3(256), 0, stream, d, vocab,

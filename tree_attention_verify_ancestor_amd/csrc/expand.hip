@@ -159,13 +159,6 @@ __device__ __forceinline__ void best_two(const float (&x)[EPT], float after_v, i
 
 // float64 sum over the wave by DPP within rows of 16 lanes, then the four row sums
 // (every lane gets the same value)
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
