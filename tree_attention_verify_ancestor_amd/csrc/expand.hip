@@ -304,7 +304,9 @@ void expand_rows_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) ml = fmaxf(ml, x[j]);
     const uint32_t lk[1] = {has ? fkey(ml) : 0u};
-    const uint32_t tw = wave_kth_key<1, 32>(lk, k);
+    // 20 key bits keep sign, exponent and 11 mantissa bits: a bound within about 1e-3
+    // relative of the exact one, for 12 fewer ballot steps; the exact ranking follows
+    const uint32_t tw = wave_kth_key<1, 20>(lk, k);
     const float mw = wave_max_f32(ml);
     const double md = (double)ml;
     double sum = 0.0;
