@@ -684,9 +684,10 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       // core is fed from two waves (one wave alone issues products at about 3/4 of the
       // peak rate).
       //
-      // Stage x is opened (its DMAs waited for, then one barrier) just before the first
-      // read of its K.  At that barrier every wave has finished its reads of stage x-2,
-      // whose buffer is then refilled with stage x+2 (stages 0..NBUF-1 were issued above).
+      // Stage x+1 is opened (its DMAs waited for, then one barrier) when stage x starts,
+      // before any read of its K.  At that barrier every wave has finished its reads of
+      // stage x-1, whose buffer is then refilled with stage x+3 (stages 0..NBUF-1 were
+      // issued above; opening stage y issues stage y+2 from y = 2 on).
       auto nsub = [&](int st) {
         const int kb0 = stage_kbase(st);
         const int ke = (has_tree && st == 0) ? n : c1;
@@ -714,15 +715,12 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         // One subtile s, in two phases whose issue order is pinned by scheduling fences:
         //  1. the products of subtile s+1 (S^T = K Q^T from kr), each with its share of
         //     the weights of s (fma, exp2, bf16 conversion) and two of the V^T reads of s;
-        //  2. O^T += V^T P^T of s; with KREAD each product with one K read of subtile
-        //     s+2 (st2, sub2) into kr (else the caller reads it after the step, behind
-        //     the barrier that opens its stage).  The row sum adds the float32 weights in
-        //     phase 1.
+        //  2. O^T += V^T P^T of s, each product with one K read of subtile s+2 (st2,
+        //     sub2) into kr.  The row sum adds the float32 weights in phase 1.
         // Where s+1 or s+2 does not exist, valid LDS data is read and the result dropped.
-        auto step = [&](auto masked_tag, auto kread_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub,
-                        int st2, int sub2) __attribute__((always_inline)) {
+        auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, int st2,
+                        int sub2) __attribute__((always_inline)) {
           constexpr bool MASKED = decltype(masked_tag)::value;
-          constexpr bool KREAD = decltype(kread_tag)::value;
           constexpr int EPG = 16 / DS;             // weights per product of the next subtile
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
           const char* kb = smem + k_tile(st);
@@ -738,17 +736,28 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
           bf16x2 pk[8];
           float psum = 0.f;
           __builtin_amdgcn_sched_barrier(0);
+          // Empty asm operands pin each slot's vector work between its fences: the
+          // scores enter in their slot and the weights, packed pairs and row sum leave
+          // it (pure arithmetic otherwise moves freely across the fences, and the
+          // optimiser gathers all of it behind the last product).
 #pragma unroll
           for (int i = 0; i < DS; ++i) {
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr.v[i], qop[0][i], sn, 0, 0, 0);
 #pragma unroll
-            for (int j = i * EPG; j < (i + 1) * EPG; ++j)
-              e[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[j], a.sl2, -msub));
+            for (int j = i * EPG; j < (i + 1) * EPG; ++j) {
+              float sv = s_cur[j];
+              asm volatile("" : "+v"(sv));
+              e[j] = __builtin_amdgcn_exp2f(fmaf(sv, a.sl2, -msub));
+              asm volatile("" : "+v"(e[j]));
+            }
             if (i > 0) {
 #pragma unroll
               for (int j = (i - 1) * EPG; j < i * EPG; j += 2) {
                 pk[j >> 1] = bf16x2{(__bf16)e[j], (__bf16)e[j + 1]};
                 psum += e[j] + e[j + 1];              // the row sum of the float32 weights
+                uint32_t pku = __builtin_bit_cast(uint32_t, pk[j >> 1]);
+                asm volatile("" : "+v"(pku), "+v"(psum));
+                pk[j >> 1] = __builtin_bit_cast(bf16x2, pku);
               }
             }
             {
@@ -782,22 +791,19 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
               o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[ks][dt], pb[ks], o[0][dt], 0, 0, 0);
-              if constexpr (KREAD) {
-                const int kx = ks * DT + dt;
-                kr.v[kx] = *(lds_bf16x8*)(uintptr_t)(ka0 ^ (kx << 5));
-              }
+              const int kx = ks * DT + dt;
+              kr.v[kx] = *(lds_bf16x8*)(uintptr_t)(ka0 ^ (kx << 5));
               __builtin_amdgcn_sched_barrier(0);
             }
           s_nxt = sn;
         };
         constexpr ic<0> unmasked{};
         constexpr ic<1> masked{};
-        constexpr ic<0> no_kread{};
-        constexpr ic<1> kread{};
 
         // subtile 0: its scores set the reference (the root is visible to every row in
-        // the tree stage; every key of a prefix stage is)
+        // the tree stage; every key of a prefix stage is).  Stage 1 opens with stage 0.
         open_stage(0);
+        if (nst > 1) open_stage(1);
         read_k(0, 0);
         sa = qk(ic<0>{}, kr);
         if (has_tree || n_full == 0)
@@ -811,39 +817,35 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
           const bool two1 = more && nsub(1) >= 2;          // stage 1 holds a second subtile
           if (nsub(0) == 2) {
             read_k(0, 1);
-            step(unmasked, no_kread, sa, sb, 0, 0, 0, 0);
-            if (more) open_stage(1);
-            read_k(more ? 1 : 0, 0);
-            step(masked, kread, sb, sa, 0, 1, two1 ? 1 : 0, 1);
+            step(unmasked, sa, sb, 0, 0, more ? 1 : 0, 0);
+            step(masked, sb, sa, 0, 1, two1 ? 1 : 0, 1);
           } else {
-            if (more) open_stage(1);
             read_k(more ? 1 : 0, 0);
-            step(unmasked, kread, sa, sb, 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
+            step(unmasked, sa, sb, 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
             sa = sb;
           }
           x = 1;
         } else if (nsub(0) >= 2) {
           read_k(0, 1);
         }
-        // full prefix stages: two unmasked subtiles each, the barrier that opens the next
-        // stage between them; one code path (where there is no next stage the K reads
-        // repeat this stage's)
+        // full prefix stages: two unmasked subtiles each.  The next stage opens first, so
+        // that both steps read the K of the subtile after next while their products run;
+        // one code path (where there is no next stage the K reads repeat this stage's)
         const int full_end = has_tree + n_full;
         for (; x < full_end; ++x) {
           const bool more = x + 1 < nst;
           const bool two = more && nsub(x + 1) >= 2;
-          step(unmasked, no_kread, sa, sb, x, 0, x, 0);
-          if (more) open_stage(x + 1);
-          read_k(more ? x + 1 : x, 0);
-          step(unmasked, kread, sb, sa, x, 1, two ? x + 1 : x, 1);
+          if (x >= 1 && more) open_stage(x + 1);
+          step(unmasked, sa, sb, x, 0, more ? x + 1 : x, 0);
+          step(unmasked, sb, sa, x, 1, two ? x + 1 : x, 1);
         }
         // a partial last prefix stage (masked; opened by the loop or above)
         if (x < nst) {
           if (nsub(x) >= 2) {
-            step(masked, kread, sa, sb, x, 0, x, 0);
-            step(masked, kread, sb, sa, x, 1, x, 1);
+            step(masked, sa, sb, x, 0, x, 0);
+            step(masked, sb, sa, x, 1, x, 1);
           } else {
-            step(masked, kread, sa, sb, x, 0, x, 0);
+            step(masked, sa, sb, x, 0, x, 0);
           }
         }
         // weights past the fixed reference's range show in the row sum (all terms are
