@@ -716,13 +716,15 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         //  1. the products of subtile s+1 (S^T = K Q^T from kr), each with its share of
         //     the weights of s (fma, exp2, bf16 conversion) and two of the V^T reads of s;
         //  2. O^T += V^T P^T of s, each product with one K read of subtile s+2 (st2,
-        //     sub2) into kr.  The row sum adds the float32 weights in phase 1.
+        //     sub2) into kr.  The row sum adds the bf16 weights the products use
+        //     (fdot2 on the packed pairs) in phase 1.
         // Where s+1 or s+2 does not exist, valid LDS data is read and the result dropped.
         auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, int st2,
                         int sub2) __attribute__((always_inline)) {
           constexpr bool MASKED = decltype(masked_tag)::value;
           constexpr int EPG = 16 / DS;             // weights per product of the next subtile
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
           const char* kb = smem + k_tile(st);
           const uint32_t va0 = lds_addr(kb + v_tile(st)) + sub * 32 * ROWB + voff0;
           if constexpr (MASKED) {
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
               for (int j = (i - 1) * EPG; j < i * EPG; j += 2) {
                 pk[j >> 1] = bf16x2{(__bf16)e[j], (__bf16)e[j + 1]};
-                psum += e[j] + e[j + 1];              // the row sum of the float32 weights
+                psum = __builtin_amdgcn_fdot2_f32_bf16(pk[j >> 1], one2, psum, false);
                 uint32_t pku = __builtin_bit_cast(uint32_t, pk[j >> 1]);
                 asm volatile("" : "+v"(pku), "+v"(psum));
                 pk[j >> 1] = __builtin_bit_cast(bf16x2, pku);
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
           for (int j = (DS - 1) * EPG; j < 16; j += 2) {
             pk[j >> 1] = bf16x2{(__bf16)e[j], (__bf16)e[j + 1]};
-            psum += e[j] + e[j + 1];
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pk[j >> 1], one2, psum, false);
           }
           l_run[0] += psum;
           bf16x8 pb[2];
