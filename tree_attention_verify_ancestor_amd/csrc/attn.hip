@@ -677,12 +677,12 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       if (p < nst && p < NBUF + extra) issue(p);
     if constexpr (WQ == 8 && WK == 1 && QT == 1) {
       // ---- eight waves of one row tile: software-pipelined over 32-key subtiles.
-      // While a wave's softmax of subtile s runs on the vector ALUs, the products of
-      // subtile s+1 (S^T = K Q^T) run on the matrix core; then O^T += V^T P^T of subtile
-      // s with the row sums beside it, and K of subtile s+2 is read from LDS while those
-      // products run.  Both waves of a SIMD issue the same mixed stream, so the matrix
-      // core is fed from two waves (one wave alone issues products at about 3/4 of the
-      // peak rate).
+      // While a wave's softmax of subtile s (with its row sums) runs on the vector ALUs,
+      // the products of subtile s+1 (S^T = K Q^T) run on the matrix core; then O^T +=
+      // V^T P^T of subtile s, and K of subtile s+2 is read from LDS while those products
+      // run.  Both waves of a SIMD issue the same mixed stream, so the matrix core is fed
+      // from two waves; a wave's LDS reads hold up its vector instructions, and together
+      // they, not the products, set the pace.
       //
       // Stage x+1 is opened (its DMAs waited for, then one barrier) when stage x starts,
       // before any read of its K.  At that barrier every wave has finished its reads of
