@@ -349,16 +349,13 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   if (one_pass) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) mine += (int)(u1[j] >= T0 && j * kCandSelThreads + tid < V);
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int tt = __shfl_up(incl, o);
-      incl += lane >= o ? tt : 0;
-    }
+    static_assert(kBatch < 64, "per-thread counts fit six bits");
+    int wtot;
+    const int pre = wave_prefix_small<6>(mine, wtot);
     int wbase = 0;
-    if (lane == kWave - 1) wbase = atomicAdd(&s_n, incl);
-    wbase = __shfl(wbase, kWave - 1);
-    int slot = wbase + incl - mine;
+    if (lane == 0) wbase = atomicAdd(&s_n, wtot);
+    wbase = __builtin_amdgcn_readfirstlane(wbase);
+    int slot = wbase + pre;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int v = j * kCandSelThreads + tid;

@@ -548,18 +548,14 @@ __device__ __forceinline__ bool wave_topk_of_lists(int len, Val value, Id id_at,
 #pragma unroll
   for (int j = 0; j < kTopKMax; ++j) cnt += (int)(j < len && rank_key(value(j), id_at(j)) >= T);
   // this lane's candidates go to buf[first ..], first = the counts of the lanes below
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    incl += lane >= o ? t : 0;
-  }
-  const int n = __builtin_amdgcn_readlane(incl, kWave - 1);
+  // (cnt <= kTopKMax < 32); the places past cnt store into the spare word buf[kWave]
+  // (T was read from it above), so that the stores need no branches
+  static_assert(kTopKMax < 32, "counts fit five bits");
+  int n;
+  const int first = wave_prefix_small<5>(cnt, n);
   if (n > kWave) return false;
-  const int first = incl - cnt;
 #pragma unroll
-  for (int j = 0; j < kTopKMax; ++j)
-    if (j < cnt) buf[first + j] = rank_key(value(j), id_at(j));
+  for (int j = 0; j < kTopKMax; ++j) buf[j < cnt ? first + j : kWave] = rank_key(value(j), id_at(j));
   wave_lds_sync();
   if (lane < n) {
     const uint64_t key = buf[lane];
@@ -831,14 +827,11 @@ __global__ __launch_bounds__(kSelThreads) void expand_select_kernel(
         int ties = 0;
         for (int j = 0; j < seg; ++j)
           if (cs + j < count && s_key[cs + j] == T) ++ties;
-        int incl = ties;
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int t = __shfl_up(incl, o);
-          if (lane >= o) incl += t;
-        }
-        if (lane == kWave - 1) s_wtot[wave] = incl;
+        static_assert(kPoolMax <= 7 * kSelThreads, "per-thread tie counts fit three bits");
+        int wties;
+        int rank = wave_prefix_small<3>(ties, wties);
+        if (lane == 0) s_wtot[wave] = wties;
         __syncthreads();
-        int rank = incl - ties;
         for (int w = 0; w < wave; ++w) rank += s_wtot[w];
         for (int j = 0; j < seg; ++j) {
           const int c = cs + j;

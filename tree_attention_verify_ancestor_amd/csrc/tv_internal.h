@@ -31,6 +31,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Exclusive prefix sum over the lanes below of a small count 0 <= x < 2^BITS, and the
+// wave's total, one ballot per bit: no lane exchanges data (a shuffle scan takes six
+// dependent LDS-permute round trips).
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int x, int& total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const uint64_t m = __ballot((x >> b) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    tot += __popcll(m) << b;
+  }
+  total = tot;
+  return pre;
+}
+
 // a float64 moved across lanes by DPP (both halves with the same control; every lane
 // in a row must be active for the patterns used here)
 template <int CTRL>
