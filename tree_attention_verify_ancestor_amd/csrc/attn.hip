@@ -706,33 +706,53 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       if (!wave_live) {
         for (int x = 0; x < nst; ++x) open_stage(x);
       } else {
-        KOps kr;                                  // K operands of the next subtile
+        bf16x8 kb[3];                             // K slices of the next subtile: a ring of three
+        VOps vr;                                  // V^T operands of the current subtile
         f32x16 sa, sb;                            // scores of the current / next subtile
-        auto read_k = [&](int st, int sub) __attribute__((always_inline)) {
-          kr = load_k(smem + k_tile(st), sub);
-        };
         float msub = 0.f;                         // the row's fixed reference
-        // One subtile s, in two phases whose issue order is pinned by scheduling fences:
-        //  1. the products of subtile s+1 (S^T = K Q^T from kr), each with its share of
-        //     the weights of s (fma, exp2, bf16 conversion) and two of the V^T reads of s;
-        //  2. O^T += V^T P^T of s, each product with one K read of subtile s+2 (st2,
-        //     sub2) into kr.  The row sum adds the bf16 weights the products use
-        //     (fdot2 on the packed pairs) in phase 1.
+        auto k_addr = [&](int st, int sub) {
+          return lds_addr(smem + k_tile(st)) + sub * 32 * ROWB + koff0;
+        };
+        auto v_addr = [&](int st, int sub) {
+          return lds_addr(smem + k_tile(st) + v_tile(st)) + sub * 32 * ROWB + voff0;
+        };
+        auto read_k_slice = [&](uint32_t ka0, int i) __attribute__((always_inline)) {
+          return *(lds_bf16x8*)(uintptr_t)(ka0 ^ (i << 5));
+        };
+        // V^T operand (ks, dt) of the subtile at va0: rows 0-7 and 8-15 of its 16-key step
+        auto read_v_op = [&](uint32_t va0, int ks, int dt) __attribute__((always_inline)) {
+          const uint32_t lo_a = (va0 ^ (dt << 6)) + ks * 16 * ROWB;
+          const uint32_t hi_a = ((va0 ^ (dt << 6)) ^ VHI) + 8 * ROWB + ks * 16 * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)lo_a);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)hi_a);
+          const s16x4 both[2] = {lo, hi};
+          vr.v[ks][dt] = *(const bf16x8*)both;
+        };
+        // One subtile s, in two phases whose issue order is pinned by scheduling fences.
+        // A wave's LDS reads hold up its vector instructions, so the softmax goes beside
+        // products with as few reads as possible:
+        //  1. the products of subtile s+1 (S^T = K Q^T), each with its share of the
+        //     weights of s (fma, exp2, bf16 conversion, row sum by fdot2); the K slices of
+        //     s+1 (st1, sub1) pass through a ring of three, each read two products ahead
+        //     (the first two were read in the previous step);
+        //  2. O^T += V^T P^T of s, each product followed by the reload of its V^T operand
+        //     with subtile s+1's, and the last two by the first two K slices of s+2
+        //     (st2, sub2).
         // Where s+1 or s+2 does not exist, valid LDS data is read and the result dropped.
-        auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, int st2,
-                        int sub2) __attribute__((always_inline)) {
+        auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, int st1,
+                        int sub1, int st2, int sub2) __attribute__((always_inline)) {
           constexpr bool MASKED = decltype(masked_tag)::value;
           constexpr int EPG = 16 / DS;             // weights per product of the next subtile
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
           const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-          const char* kb = smem + k_tile(st);
-          const uint32_t va0 = lds_addr(kb + v_tile(st)) + sub * 32 * ROWB + voff0;
           if constexpr (MASKED) {
             const bool tree = has_tree && st == 0;
             apply_mask(s_cur, stage_kbase(st) + sub * 32 + 4 * g, tree ? n : c1,
                        tree ? qanc[0] : ~0ull);
           }
-          VOps v;
+          const uint32_t ka1 = k_addr(st1, sub1);
+          const uint32_t va1 = v_addr(st1, sub1);
+          const uint32_t ka2 = k_addr(st2, sub2);
           f32x16 sn = f32x16{};
           float e[16];
           bf16x2 pk[8];
@@ -744,7 +764,8 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
           // optimiser gathers all of it behind the last product).
 #pragma unroll
           for (int i = 0; i < DS; ++i) {
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr.v[i], qop[0][i], sn, 0, 0, 0);
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % 3], qop[0][i], sn, 0, 0, 0);
+            if (i + 2 < DS) kb[(i + 2) % 3] = read_k_slice(ka1, i + 2);
 #pragma unroll
             for (int j = i * EPG; j < (i + 1) * EPG; ++j) {
               float sv = s_cur[j];
@@ -762,16 +783,6 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
                 pk[j >> 1] = __builtin_bit_cast(bf16x2, pku);
               }
             }
-            {
-              // V^T operand (ks, dt) = i: rows 0-7 and 8-15 of its 16-key step
-              const int ks = i / DT, dt = i % DT;
-              const uint32_t lo_a = (va0 ^ (dt << 6)) + ks * 16 * ROWB;
-              const uint32_t hi_a = ((va0 ^ (dt << 6)) ^ VHI) + 8 * ROWB + ks * 16 * ROWB;
-              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)lo_a);
-              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)hi_a);
-              const s16x4 both[2] = {lo, hi};
-              v.v[ks][dt] = *(const bf16x8*)both;
-            }
             __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
@@ -786,15 +797,15 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
             pb[j >> 2][2 * (j & 3)] = pk[j][0];
             pb[j >> 2][2 * (j & 3) + 1] = pk[j][1];
           }
-          const uint32_t ka0 = lds_addr(smem + k_tile(st2)) + sub2 * 32 * ROWB + koff0;
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-              o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[ks][dt], pb[ks], o[0][dt], 0, 0, 0);
-              const int kx = ks * DT + dt;
-              kr.v[kx] = *(lds_bf16x8*)(uintptr_t)(ka0 ^ (kx << 5));
+              o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr.v[ks][dt], pb[ks], o[0][dt], 0, 0, 0);
+              read_v_op(va1, ks, dt);
+              const int q = ks * DT + dt;
+              if (q >= 2 * DT - 2) kb[q - (2 * DT - 2)] = read_k_slice(ka2, q - (2 * DT - 2));
               __builtin_amdgcn_sched_barrier(0);
             }
           s_nxt = sn;
@@ -806,48 +817,60 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         // the tree stage; every key of a prefix stage is).  Stage 1 opens with stage 0.
         open_stage(0);
         if (nst > 1) open_stage(1);
-        read_k(0, 0);
-        sa = qk(ic<0>{}, kr);
+        sa = qk(ic<0>{}, load_k(smem + k_tile(0), 0));
         if (has_tree || n_full == 0)
           apply_mask(sa, stage_kbase(0) + 4 * g, has_tree ? n : c1, has_tree ? qanc[0] : ~0ull);
         reference(ic<0>{}, sa);
         msub = m_run[0] == -INFINITY ? 0.f : m_run[0];
+        {
+          const uint32_t va0 = v_addr(0, 0);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) read_v_op(va0, ks, dt);
+        }
+        // the first two K slices of subtile 1
+        auto prefetch_k = [&](int st, int sub) __attribute__((always_inline)) {
+          const uint32_t ka = k_addr(st, sub);
+          kb[0] = read_k_slice(ka, 0);
+          kb[1] = read_k_slice(ka, 1);
+        };
         int x = 0;
         if (has_tree) {
           // the tree stage: one or two masked subtiles (the first one masked already)
           const bool more = nst > 1;
           const bool two1 = more && nsub(1) >= 2;          // stage 1 holds a second subtile
           if (nsub(0) == 2) {
-            read_k(0, 1);
-            step(unmasked, sa, sb, 0, 0, more ? 1 : 0, 0);
-            step(masked, sb, sa, 0, 1, two1 ? 1 : 0, 1);
+            prefetch_k(0, 1);
+            step(unmasked, sa, sb, 0, 0, 0, 1, more ? 1 : 0, 0);
+            step(masked, sb, sa, 0, 1, more ? 1 : 0, more ? 0 : 1, two1 ? 1 : 0, 1);
           } else {
-            read_k(more ? 1 : 0, 0);
-            step(unmasked, sa, sb, 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
+            prefetch_k(more ? 1 : 0, 0);
+            step(unmasked, sa, sb, 0, 0, more ? 1 : 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
             sa = sb;
           }
           x = 1;
-        } else if (nsub(0) >= 2) {
-          read_k(0, 1);
+        } else {
+          prefetch_k(0, nsub(0) >= 2 ? 1 : 0);
         }
         // full prefix stages: two unmasked subtiles each.  The next stage opens first, so
-        // that both steps read the K of the subtile after next while their products run;
-        // one code path (where there is no next stage the K reads repeat this stage's)
+        // that the steps can read its K and V^T while their products run; one code path
+        // (where there is no next stage the reads repeat this stage's)
         const int full_end = has_tree + n_full;
         for (; x < full_end; ++x) {
           const bool more = x + 1 < nst;
           const bool two = more && nsub(x + 1) >= 2;
           if (x >= 1 && more) open_stage(x + 1);
-          step(unmasked, sa, sb, x, 0, more ? x + 1 : x, 0);
-          step(unmasked, sb, sa, x, 1, two ? x + 1 : x, 1);
+          step(unmasked, sa, sb, x, 0, x, 1, more ? x + 1 : x, 0);
+          step(unmasked, sb, sa, x, 1, more ? x + 1 : x, more ? 0 : 1, two ? x + 1 : x, 1);
         }
         // a partial last prefix stage (masked; opened by the loop or above)
         if (x < nst) {
           if (nsub(x) >= 2) {
-            step(masked, sa, sb, x, 0, x, 0);
-            step(masked, sb, sa, x, 1, x, 1);
+            step(masked, sa, sb, x, 0, x, 1, x, 0);
+            step(masked, sb, sa, x, 1, x, 1, x, 1);
           } else {
-            step(masked, sa, sb, x, 0, x, 0);
+            step(masked, sa, sb, x, 0, x, 0, x, 0);
           }
         }
         // weights past the fixed reference's range show in the row sum (all terms are
