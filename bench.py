@@ -349,7 +349,7 @@ def gpu_leg(args, inp):
     h_c = rnd((rows_c, dc), 1.0)
     lg_c = torch.empty((rows_c, Vc), dtype=torch.float32, device=dev)
     cd_c = torch.empty((rows_c, Cc), dtype=torch.int32, device=dev)
-    ws_c = torch.empty((tv.lib().tree_candidate_workspace_size(rows_c, rc),), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty((tv.lib().tree_candidate_workspace_size(rows_c, rc, Vc),), dtype=torch.uint8, device=dev)
     run_c = lambda fa: tv.tree_candidate_logits(h_c, fa[0], fa[1], W_c, Cc, logits=lg_c, cand=cd_c, ws=ws_c)
     with torch.cuda.stream(side):
         run_c(facs[0])

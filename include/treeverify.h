@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TV_ABI_VERSION 1
+#define TV_ABI_VERSION 2
 #define TV_MAX_NODES 64
 
 typedef enum {
@@ -176,13 +176,13 @@ tv_status tree_draft_continue(const void* ws, size_t ws_bytes, int B, int k, int
  * Each dot product is a float64 sum of the exact products, rounded once to float32.
  * The rows feed tree_expand_rerank unchanged (their log-sum-exp, top-k and scores).
  * Outputs: logits fp32 [rows][vocab], cand int32 [rows][C].  All device pointers,
- * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r) bytes (z in float64,
- * rows padded to whole groups of 16), no
- * initialisation needed.
+ * 16-byte aligned inputs; ws: tree_candidate_workspace_size(rows, r, vocab) bytes (z in
+ * float64, rows padded to whole groups of 16, then one uint32 score maximum per row and
+ * group of 16 or 32 tokens), no initialisation needed.
  * Limits: d % 8 == 0, r % 32 == 0, 32 <= r <= 512, 1 <= C <= 256, C <= vocab.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED (alignment), TV_ERR_WORKSPACE.
  */
-size_t tree_candidate_workspace_size(int rows, int r);
+size_t tree_candidate_workspace_size(int rows, int r, int vocab);
 tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C, const void* h,
                                 const void* A, const void* Bm, const void* W, float* logits,
                                 int32_t* cand, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -24,7 +24,7 @@ static int g_fail = 0;
 int main() {
   char buf[4096] __attribute__((aligned(16)));
   void* P = buf;                                   // a non-null, aligned stand-in, never read
-  CHECK(tv_abi_version() == 1);
+  CHECK(tv_abi_version() == 2);
   for (int s = 0; s <= 6; ++s) CHECK(tv_status_string((tv_status)s) != nullptr);
 
   // tree_build / tree_accept argument checks
@@ -91,9 +91,11 @@ int main() {
   CHECK(tree_accept_stochastic(1, 64, 0, (int32_t*)P, (uint64_t*)P, (int32_t*)P, (int32_t*)P, (float*)P,
                                (float*)P, (float*)P, (float*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P,
                                nullptr, nullptr) == TV_ERR_SHAPE);
-  CHECK(tree_candidate_workspace_size(4, 513) == 0);
-  const size_t cws = tree_candidate_workspace_size(4, 64);
+  CHECK(tree_candidate_workspace_size(4, 513, 1000) == 0);
+  CHECK(tree_candidate_workspace_size(4, 64, 0) == 0);
+  const size_t cws = tree_candidate_workspace_size(4, 64, 1000);
   CHECK(cws > 0);
+  for (int V : {1, 15, 16, 17, 32000, 128256, 1 << 24}) CHECK(tree_candidate_workspace_size(16, 512, V) > 0);
   CHECK(tree_candidate_logits(4, 12, 64, 1000, 8, P, P, P, P, (float*)P, (int32_t*)P, P, cws, nullptr) ==
         TV_ERR_SHAPE);
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_identity(L):
-    assert L.tv_abi_version() == 1
+    assert L.tv_abi_version() == 2
     assert L.tv_status_string(0) == b"ok"
     assert b"workspace" in L.tv_status_string(WS)
 
@@ -101,9 +101,12 @@ def test_draft_continue_validation(L):
 
 
 def test_candidate_logits_validation(L):
-    need = L.tree_candidate_workspace_size(4, 64)
-    assert need >= 4 * 64 * 4 and need % 256 == 0
-    assert L.tree_candidate_workspace_size(4, 513) == 0
+    need = L.tree_candidate_workspace_size(4, 64, 1000)
+    # z (16 padded rows x r float64) then one uint32 maximum per row and 16-token group
+    assert need == 16 * 64 * 8 + (4 * 63 * 4 + 255) // 256 * 256
+    assert L.tree_candidate_workspace_size(4, 513, 1000) == 0
+    assert L.tree_candidate_workspace_size(4, 64, 0) == 0
+    assert L.tree_candidate_workspace_size(4, 64, 128256) > L.tree_candidate_workspace_size(4, 64, 32000)
     f = lambda rows=4, d=128, r=64, V=1000, C=8, h=P, ws=P, ws_bytes=need: L.tree_candidate_logits(
         rows, d, r, V, C, h, P, P, P, P, P, ws, ws_bytes, Z)
     assert f(h=Z) == NULL

@@ -42,7 +42,7 @@ _SIGNATURES = {
     "tree_accept_stochastic": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P]),
     "tree_kv_compact": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
-    "tree_candidate_workspace_size": (_S, [_I, _I]),
+    "tree_candidate_workspace_size": (_S, [_I, _I, _I]),
     "tree_candidate_logits": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
 }
 

@@ -23,11 +23,13 @@
 //                      logits rows.  At 10 rows this is about 10 flops per Bm byte, the
 //                      float64 ridge of the vector ALUs, so exact sums cost about the
 //                      HBM time.
-//   cand_select_kernel one workgroup per row: the C-th largest of 256 group maxima
-//                      (groups of four threads' strided tokens) bounds the C-th best
-//                      score from below; the few scores at or above it are gathered in
-//                      LDS and ranked there (ties to the lower id); with heavy ties,
-//                      radix selection over the whole row on order-preserving keys
+//   cand_select_kernel one workgroup per row: the C-th largest of the score groups'
+//                      maxima (one group per score wave, recorded by the score kernel)
+//                      bounds the C-th best score from below; only the groups whose
+//                      maximum reaches the bound are read, their scores at or above it
+//                      gathered in LDS and ranked there (ties to the lower id); with
+//                      heavy ties, radix selection over the whole row on
+//                      order-preserving keys
 //   cand_exact_kernel  one wave per (row, candidate): its exact logit overwrites the
 //                      score
 // HBM traffic: Bm (V*r*2 B) once per group of 16 rows, the C rows of W per draft row
@@ -43,6 +45,9 @@ constexpr int kScoreWaves = 4;                 // waves per score workgroup
 constexpr int kCandSelThreads = 1024;
 constexpr int kCandGather = 2048;              // keys above the lower bound ranked in LDS
 constexpr int kCandGroups = kCandSelThreads / 4;   // groups of four threads for the lower bound
+constexpr int kMinTokW = 16;                   // the fewest tokens a score wave covers
+constexpr int kGmaxPerThread = 8;              // score-group maxima per selection thread
+constexpr int kCandQualMax = 512;              // score groups read by the bounded selection
 
 // Order-preserving map of a float to an unsigned key: a larger value has a larger key,
 // -0 and +0 share one key.
@@ -103,10 +108,24 @@ __global__ __launch_bounds__(256) void cand_z_kernel(int rows, int d, int r, con
 // 16-byte read giving two rows of one j, shared by the TPT tokens.  Each token's sum: a
 // lane's j in increasing order, then the eight lanes combined by neighbours, pairs, then
 // halves -- one fixed order.
+// The largest of a wave's 64 keys, in every lane (keys >= 0; quad, half-row and row
+// steps by DPP, then the four rows by readlane)
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// Besides the scores, each wave records, per row, the largest key (cand_key) of its
+// 8 * TPT tokens (a score group) in gmax[row][group], group = the wave's index in the
+// grid; tokens past the vocabulary count as key 0.
 template <int ROWS, int TPT, int RMAX>
 __global__ __launch_bounds__(kScoreWaves * kWave) void cand_score_kernel(
     int rows, int r, int V, const __bf16* __restrict__ Bm, const double* __restrict__ z64,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, uint32_t* __restrict__ gmax, int ng) {
   static_assert(ROWS % 2 == 0 && ROWS <= kCandGroup, "rows in pairs, at most one group");
   constexpr int kQMax = (RMAX + 63) / 64;             // chunks per lane at most
   // lane part p's z: zs[p * kPart + (q * 8 + e) * ROWS + row] = z[row][(8q + p) * 8 + e];
@@ -222,10 +241,23 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void cand_score_kernel(
       if ((i & 7) == p && row < rows && v < V) logits[(size_t)row * V + v] = (float)acc[u][i];
     }
   }
+  // the wave's score group: the largest key of each row over its tokens
+  const int grp = blockIdx.x * kScoreWaves + wave;
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+      m = max(m, tw0 + t + 8 * u < V ? cand_key((float)acc[u][i]) : 0u);
+    m = wave_max_key(m);
+    const int row = g * kCandGroup + i;
+    if (lane == 0 && row < rows && grp < ng) gmax[(size_t)row * ng + grp] = m;
+  }
 }
 
 __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
-    int V, int C, const float* __restrict__ logits, int32_t* __restrict__ cand) {
+    int V, int C, const float* __restrict__ logits, const uint32_t* __restrict__ gmax, int ng,
+    int tokw, int32_t* __restrict__ cand) {
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -238,6 +270,8 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
   __shared__ int s_ids[kCandMaxC];
   __shared__ uint32_t s_keys[kCandMaxC];
   __shared__ int s_rank[kCandMaxC];
+  __shared__ int s_grp[kCandQualMax];
+  __shared__ int s_nq;
 
   // every pass over the row: 32 coalesced key loads per thread in flight, then the
   // body for each (id, key)
@@ -313,6 +347,113 @@ __global__ __launch_bounds__(kCandSelThreads) void cand_select_kernel(
       __syncthreads();
     }
   };
+
+  // rank the gathered keys by (larger key, lower id); the first C are the candidates
+  auto rank_gathered = [&](int n_ge) {
+    for (int gi = tid; gi < n_ge; gi += kCandSelThreads) {
+      const uint64_t km = s_gk[gi];
+      int rk = 0;
+#pragma unroll 8
+      for (int o = 0; o < n_ge; ++o) rk += (int)(s_gk[o] > km);
+      if (rk < C) s_rank[rk] = (int)~(uint32_t)km;
+    }
+    __syncthreads();
+    if (tid < C) cand[(size_t)row * C + tid] = s_rank[tid];
+  };
+
+  // Bounded by the score groups' maxima (written by the score kernel): T0 = the leading
+  // 16 bits of the C-th largest group maximum.  C distinct scores (the C largest group
+  // maxima) are >= T0, so every one of the C best scores is too, and only a group whose
+  // maximum is >= T0 can hold one: those groups are read, their keys >= T0 gathered in
+  // LDS and ranked.  Usually about C groups of tokw tokens, instead of the whole row.
+  // Too many such groups or keys (heavy ties) fall through to the exact selection below.
+  // The bound needs at least C groups (fewer than C groups: the path further down).
+  bool bounded = gmax != nullptr && ng >= C && ng <= kGmaxPerThread * kCandSelThreads;
+  if (bounded) {
+    uint32_t gm[kGmaxPerThread];
+#pragma unroll
+    for (int j = 0; j < kGmaxPerThread; ++j) {
+      const int gi = j * kCandSelThreads + tid;
+      gm[j] = gmax[(size_t)row * ng + min(gi, ng - 1)];
+      gm[j] = gi < ng ? gm[j] : 0u;
+    }
+    if (tid == 0) {
+      s_nq = 0;
+      s_n = 0;
+    }
+    uint32_t T0;
+    int need0;
+    radix_select([&](auto&& body) {
+#pragma unroll
+      for (int j = 0; j < kGmaxPerThread; ++j)
+        if (j * kCandSelThreads + tid < ng) body(0, gm[j]);
+    }, C, T0, need0, 2);
+    // the qualifying groups into s_grp: per-thread counts, a ballot scan, one atomic per wave
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < kGmaxPerThread; ++j) mine += (int)(gm[j] >= T0 && j * kCandSelThreads + tid < ng);
+    int wtot;
+    const int pre = wave_prefix_small<4>(mine, wtot);
+    int wbase = 0;
+    if (lane == 0 && wtot > 0) wbase = atomicAdd(&s_nq, wtot);
+    int slot = __builtin_amdgcn_readfirstlane(wbase) + pre;
+#pragma unroll
+    for (int j = 0; j < kGmaxPerThread; ++j) {
+      const int gi = j * kCandSelThreads + tid;
+      if (gm[j] >= T0 && gi < ng) {
+        if (slot < kCandQualMax) s_grp[slot] = gi;
+        ++slot;
+      }
+    }
+    __syncthreads();
+    const int nq = s_nq;
+    bounded = nq <= kCandQualMax;
+    if (bounded) {
+      // their tokens, kGB per thread in flight, keys >= T0 gathered by ballot scans
+      constexpr int kGB = 4;
+      const int ntok = nq * tokw;
+      for (int base = 0; base < ntok; base += kGB * kCandSelThreads) {
+        int vv[kGB];
+        float xv[kGB];
+#pragma unroll
+        for (int i = 0; i < kGB; ++i) {
+          const int q = base + i * kCandSelThreads + tid;
+          const int qq = min(q, ntok - 1);
+          vv[i] = s_grp[qq / tokw] * tokw + qq % tokw;
+          xv[i] = lrow[min(vv[i], V - 1)];
+          vv[i] = q < ntok && vv[i] < V ? vv[i] : -1;
+        }
+        int cnt = 0;
+        uint32_t uk[kGB];
+#pragma unroll
+        for (int i = 0; i < kGB; ++i) {
+          uk[i] = cand_key(xv[i]);
+          cnt += (int)(vv[i] >= 0 && uk[i] >= T0);
+        }
+        int wt;
+        const int pr = wave_prefix_small<3>(cnt, wt);
+        int wb = 0;
+        if (lane == 0 && wt > 0) wb = atomicAdd(&s_n, wt);
+        int sl = __builtin_amdgcn_readfirstlane(wb) + pr;
+#pragma unroll
+        for (int i = 0; i < kGB; ++i) {
+          if (vv[i] >= 0 && uk[i] >= T0) {
+            if (sl < kCandGather) s_gk[sl] = ((uint64_t)uk[i] << 32) | (uint32_t)~vv[i];
+            ++sl;
+          }
+        }
+      }
+      __syncthreads();
+      // at least C keys reach T0 (the C largest group maxima do); the test keeps every
+      // rank below C written should that ever fail
+      const int n_ge = s_n;
+      if (n_ge >= C && n_ge <= kCandGather) {
+        rank_gathered(n_ge);
+        return;
+      }
+    }
+    // heavy ties: the exact selection below
+  }
 
   // A lower bound first: the largest key of each group of four threads (their strided
   // tokens), and T0 the C-th largest of those 256 group maxima: C groups hold a key
@@ -459,36 +600,48 @@ __global__ __launch_bounds__(256) void cand_exact_kernel(int d, int V, int C,
 
 }  // namespace tv
 
-TV_API size_t tree_candidate_workspace_size(int rows, int r) {
-  if (rows < 1 || r < 1 || r > tv::kCandMaxR) return 0;
+// z64 (float64, rows padded to whole groups of 16), then the score-group maxima (one
+// uint32 key per row and group of at least kMinTokW tokens)
+static size_t cand_z_bytes(int rows, int r) {
   const size_t groups = ((size_t)rows + tv::kCandGroup - 1) / tv::kCandGroup;
   return (groups * tv::kCandGroup * r * sizeof(double) + 255) / 256 * 256;
 }
 
+TV_API size_t tree_candidate_workspace_size(int rows, int r, int vocab) {
+  if (rows < 1 || r < 1 || r > tv::kCandMaxR || vocab < 1) return 0;
+  const size_t ng = ((size_t)vocab + tv::kMinTokW - 1) / tv::kMinTokW;
+  return cand_z_bytes(rows, r) + ((size_t)rows * ng * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
 namespace tv {
+// tokens per score wave (one score group) for a number of rows
+static int score_tokens_per_wave(int rows) {
+  const int rg = rows > kCandGroup ? kCandGroup : (rows + 1) & ~1;
+  return rg <= 12 ? 32 : 16;
+}
 template <int ROWS, int RMAX>
 static void launch_score_rows(int rows, int r, int vocab, const __bf16* Bm, const double* z64,
-                              float* logits, hipStream_t stream) {
+                              float* logits, uint32_t* gmax, int ng, hipStream_t stream) {
   constexpr int TPT = ROWS <= 12 ? 4 : 2;             // tokens per lane: acc stays <= 48 doubles
   const int per_wg = kScoreWaves * 8 * TPT;
   const dim3 grid((vocab + per_wg - 1) / per_wg, (rows + kCandGroup - 1) / kCandGroup);
   hipLaunchKernelGGL((cand_score_kernel<ROWS, TPT, RMAX>), grid, dim3(kScoreWaves * kWave), 0, stream,
-                     rows, r, vocab, Bm, z64, logits);
+                     rows, r, vocab, Bm, z64, logits, gmax, ng);
 }
 template <int RMAX>
 static void launch_score(int rows, int r, int vocab, const __bf16* Bm, const double* z64,
-                         float* logits, hipStream_t stream) {
+                         float* logits, uint32_t* gmax, int ng, hipStream_t stream) {
   // the group's rows rounded up to even (whole groups of 16 past 16 rows)
   const int rg = rows > kCandGroup ? kCandGroup : (rows + 1) & ~1;
   switch (rg) {
-    case 2: launch_score_rows<2, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 4: launch_score_rows<4, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 6: launch_score_rows<6, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 8: launch_score_rows<8, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 10: launch_score_rows<10, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 12: launch_score_rows<12, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    case 14: launch_score_rows<14, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
-    default: launch_score_rows<16, RMAX>(rows, r, vocab, Bm, z64, logits, stream); break;
+    case 2: launch_score_rows<2, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 4: launch_score_rows<4, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 6: launch_score_rows<6, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 8: launch_score_rows<8, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 10: launch_score_rows<10, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 12: launch_score_rows<12, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    case 14: launch_score_rows<14, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
+    default: launch_score_rows<16, RMAX>(rows, r, vocab, Bm, z64, logits, gmax, ng, stream); break;
   }
 }
 }  // namespace tv
@@ -503,18 +656,21 @@ TV_API tv_status tree_candidate_logits(int rows, int d, int r, int vocab, int C,
     return TV_ERR_SHAPE;
   if ((((uintptr_t)h | (uintptr_t)A | (uintptr_t)Bm | (uintptr_t)W) & 15) != 0)
     return TV_ERR_UNSUPPORTED;
-  const size_t need = tree_candidate_workspace_size(rows, r);
+  const size_t need = tree_candidate_workspace_size(rows, r, vocab);
   if (!ws || ws_bytes < need) return TV_ERR_WORKSPACE;
   double* z64 = (double*)ws;
+  const int tokw = tv::score_tokens_per_wave(rows);
+  const int ng = (vocab + tokw - 1) / tokw;
+  uint32_t* gmax = (uint32_t*)((char*)ws + cand_z_bytes(rows, r));
   const int padded = (rows + tv::kCandGroup - 1) / tv::kCandGroup * tv::kCandGroup;
   hipLaunchKernelGGL(tv::cand_z_kernel, dim3((r + 3) / 4, padded), dim3(256), 0, stream, rows, d, r,
                      (const __bf16*)h, (const __bf16*)A, z64);
   if (r <= 256)
-    tv::launch_score<256>(rows, r, vocab, (const __bf16*)Bm, z64, logits, stream);
+    tv::launch_score<256>(rows, r, vocab, (const __bf16*)Bm, z64, logits, gmax, ng, stream);
   else
-    tv::launch_score<512>(rows, r, vocab, (const __bf16*)Bm, z64, logits, stream);
+    tv::launch_score<512>(rows, r, vocab, (const __bf16*)Bm, z64, logits, gmax, ng, stream);
   hipLaunchKernelGGL(tv::cand_select_kernel, dim3(rows), dim3(tv::kCandSelThreads), 0, stream,
-                     vocab, C, (const float*)logits, cand);
+                     vocab, C, (const float*)logits, (const uint32_t*)gmax, ng, tokw, cand);
   hipLaunchKernelGGL(tv::cand_exact_kernel, dim3((C + 3) / 4, rows), dim3(256), 0, stream, d, vocab,
                      C, (const __bf16*)h, (const __bf16*)W, (const int32_t*)cand, logits);
   return tv::launch_status();

@@ -140,7 +140,7 @@ def tree_candidate_logits(h, A, Bm, W, C, logits=None, cand=None, ws=None):
     if cand is None:
         cand = torch.empty((rows, C), dtype=torch.int32, device=dev)
     if ws is None:
-        ws = torch.empty((max(16, lib().tree_candidate_workspace_size(rows, r)),), dtype=torch.uint8,
+        ws = torch.empty((max(16, lib().tree_candidate_workspace_size(rows, r, vocab)),), dtype=torch.uint8,
                          device=dev)
     check("tree_candidate_logits", lib().tree_candidate_logits(
         rows, d, r, vocab, C, _ptr(h), _ptr(A), _ptr(Bm), _ptr(W), _ptr(logits), _ptr(cand),
