@@ -56,13 +56,16 @@ def _time_calls(Hq, Hkv, D, B, L, nodes, bufs, reps, device):
                 call()
         graph.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
+        # each replay timed on its own and the median kept: a host stall between two
+        # replays (the GPU idles while it lasts) then moves one sample, not the figure
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(5)]
+        for e0, e1 in ev:
+            e0.record()
             graph.replay()
-        e1.record()
+            e1.record()
         torch.cuda.synchronize()
-        res.append(e0.elapsed_time(e1) * 1e3 / (3 * reps))
+        res.append(float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3 / reps)
     return res
 
 
