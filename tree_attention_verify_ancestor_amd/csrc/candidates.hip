@@ -108,17 +108,6 @@ __global__ __launch_bounds__(256) void cand_z_kernel(int rows, int d, int r, con
 // 16-byte read giving two rows of one j, shared by the TPT tokens.  Each token's sum: a
 // lane's j in increasing order, then the eight lanes combined by neighbours, pairs, then
 // halves -- one fixed order.
-// The largest of a wave's 64 keys, in every lane (keys >= 0; quad, half-row and row
-// steps by DPP, then the four rows by readlane)
-__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
-}
-
 // Besides the scores, each wave records, per row, the largest key (cand_key) of its
 // 8 * TPT tokens (a score group) in gmax[row][group], group = the wave's index in the
 // grid; tokens past the vocabulary count as key 0.
@@ -231,27 +220,37 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void cand_score_kernel(
       a += dpp_f64<0x141>(a);
       acc[u][i] = a;
     }
-  // lane p of each group writes rows p, p + 8 of its tokens
+  // lane p of each group takes rows p and p + 8 of its tokens (selected from the sums
+  // every lane of the group holds): it writes their scores, and keeps per row the largest
+  // key (cand_key) over its tokens, tokens past the vocabulary counting as key 0
+  const int grp = blockIdx.x * kScoreWaves + wave;
+  const int row0 = g * kCandGroup + p;
+  uint32_t m0 = 0u, m1 = 0u;
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
     const int v = tw0 + t + 8 * u;
+    double x0 = acc[u][0], x1 = acc[u][ROWS > 8 ? 8 : 0];
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const int row = g * kCandGroup + i;
-      if ((i & 7) == p && row < rows && v < V) logits[(size_t)row * V + v] = (float)acc[u][i];
-    }
+    for (int i = 1; i < (ROWS < 8 ? ROWS : 8); ++i) x0 = p == i ? acc[u][i] : x0;
+#pragma unroll
+    for (int i = 9; i < ROWS; ++i) x1 = p == i - 8 ? acc[u][i] : x1;
+    const float f0 = (float)x0, f1 = (float)x1;
+    if (p < ROWS && row0 < rows && v < V) logits[(size_t)row0 * V + v] = f0;
+    if (p + 8 < ROWS && row0 + 8 < rows && v < V) logits[(size_t)(row0 + 8) * V + v] = f1;
+    m0 = max(m0, v < V ? cand_key(f0) : 0u);
+    m1 = max(m1, v < V ? cand_key(f1) : 0u);
   }
-  // the wave's score group: the largest key of each row over its tokens
-  const int grp = blockIdx.x * kScoreWaves + wave;
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u)
-      m = max(m, tw0 + t + 8 * u < V ? cand_key((float)acc[u][i]) : 0u);
-    m = wave_max_key(m);
-    const int row = g * kCandGroup + i;
-    if (lane == 0 && row < rows && grp < ng) gmax[(size_t)row * ng + grp] = m;
+  // the same p across the wave's eight token groups: lanes p + 8t, t = 0..7 (row rotate
+  // by eight, then lanes 16 and 32 apart); lane p (t = 0) writes the group maxima
+  m0 = max(m0, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m0, 0x128, 0xF, 0xF, false));
+  m1 = max(m1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m1, 0x128, 0xF, 0xF, false));
+  m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
+  m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
+  m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 32));
+  m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 32));
+  if (t == 0 && grp < ng) {
+    if (p < ROWS && row0 < rows) gmax[(size_t)row0 * ng + grp] = m0;
+    if (p + 8 < ROWS && row0 + 8 < rows) gmax[(size_t)(row0 + 8) * ng + grp] = m1;
   }
 }
 
