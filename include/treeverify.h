@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TV_ABI_VERSION 2
+#define TV_ABI_VERSION 3
 #define TV_MAX_NODES 64
 
 typedef enum {
@@ -349,18 +349,33 @@ tv_status tree_accept(int B, int n_max, const int32_t* parent, const int32_t* de
  *   u_bonus    float32 [B]         uniform in [0,1) for the bonus token
  *   accept_len, best_node, bonus_token int32 [B], path int32 [B][n_max] (nullable):
  *                 as for tree_accept
- * vocab >= 1.  Up to 36864 tokens the weights r live in LDS; past that they are
- * recomputed from p_target and q_draft on every pass over the vocabulary (same bits),
- * so each rejection streams two rows instead of one.  Tokens outside [0, vocab) fail.
- * Sums in float64 depend on their order in the last bits: a decision within ~1e-15
- * (relative) of its threshold may differ from a sequential evaluation.
+ *   ws, ws_bytes   workspace of at least tree_accept_stochastic_workspace_size(B, n_max,
+ *                  vocab) bytes, 16-byte aligned, device memory; nullable
+ * vocab >= 1.  With a workspace (and a size query above 0) each sequence's vocabulary
+ * is cut into slices, one workgroup each, that keep their slice of r and of the draft
+ * row on chip and exchange their float64 totals through the workspace after every
+ * change of r; the workgroups of one call must all be resident at once (the slices are
+ * sized so that B times their number stays within the device's compute units), and a
+ * sequence whose exchange waits past a bound (work of other streams holding the compute
+ * units) gets -1 in every output.  The workspace needs no initial contents; calls that
+ * share one must be ordered.  Without a workspace (ws NULL) one workgroup per sequence
+ * walks the tree: up to 36864 tokens with r in LDS; past that r is recomputed from
+ * p_target and q_draft on every pass over the vocabulary (same bits), so each rejection
+ * streams two rows instead of one.  Tokens outside [0, vocab) fail.  Sums in float64
+ * depend on their order in the last bits (the slices add their totals in slice order):
+ * a decision within ~1e-15 (relative) of its threshold may differ from a sequential
+ * evaluation.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_WORKSPACE (ws given but smaller than the
+ * query or misaligned), TV_ERR_HIP.
  */
+size_t tree_accept_stochastic_workspace_size(int B, int n_max, int vocab);
 tv_status tree_accept_stochastic(int B, int n_max, int vocab, const int32_t* parent,
                                  const uint64_t* anc, const int32_t* n_nodes,
                                  const int32_t* token, const float* p_target,
                                  const float* q_draft, const float* u_accept,
                                  const float* u_bonus, int32_t* accept_len, int32_t* best_node,
-                                 int32_t* bonus_token, int32_t* path, hipStream_t stream);
+                                 int32_t* bonus_token, int32_t* path, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /*
  * tree_kv_compact -- the accepted continuation's K/V into the KV cache.

@@ -24,7 +24,7 @@ static int g_fail = 0;
 int main() {
   char buf[4096] __attribute__((aligned(16)));
   void* P = buf;                                   // a non-null, aligned stand-in, never read
-  CHECK(tv_abi_version() == 2);
+  CHECK(tv_abi_version() == 3);
   for (int s = 0; s <= 6; ++s) CHECK(tv_status_string((tv_status)s) != nullptr);
 
   // tree_build / tree_accept argument checks
@@ -90,7 +90,13 @@ int main() {
   // stochastic acceptance, compaction, candidate head: argument checks
   CHECK(tree_accept_stochastic(1, 64, 0, (int32_t*)P, (uint64_t*)P, (int32_t*)P, (int32_t*)P, (float*)P,
                                (float*)P, (float*)P, (float*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P,
-                               nullptr, nullptr) == TV_ERR_SHAPE);
+                               nullptr, nullptr, 0, nullptr) == TV_ERR_SHAPE);
+  CHECK(tree_accept_stochastic(1, 64, 100, (int32_t*)P, (uint64_t*)P, (int32_t*)P, (int32_t*)P, nullptr,
+                               (float*)P, (float*)P, (float*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P,
+                               nullptr, nullptr, 0, nullptr) == TV_ERR_NULL);
+  CHECK(tree_accept_stochastic_workspace_size(0, 64, 1000) == 0);
+  CHECK(tree_accept_stochastic_workspace_size(2, 65, 1000) == 0);
+  CHECK(tree_accept_stochastic_workspace_size(2, 64, 0) == 0);
   CHECK(tree_candidate_workspace_size(4, 513, 1000) == 0);
   CHECK(tree_candidate_workspace_size(4, 64, 0) == 0);
   const size_t cws = tree_candidate_workspace_size(4, 64, 1000);

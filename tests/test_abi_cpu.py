@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_identity(L):
-    assert L.tv_abi_version() == 2
+    assert L.tv_abi_version() == 3
     assert L.tv_status_string(0) == b"ok"
     assert b"workspace" in L.tv_status_string(WS)
 
@@ -269,7 +269,7 @@ def test_kv_compact_validation(L):
 
 
 def _stoch(L, B=2, n_max=64, V=1000, p=P):
-    return L.tree_accept_stochastic(B, n_max, V, P, P, P, P, p, P, P, P, P, P, P, Z, Z)
+    return L.tree_accept_stochastic(B, n_max, V, P, P, P, P, p, P, P, P, P, P, P, Z, Z, 0, Z)
 
 
 def test_accept_stochastic_validation(L):
@@ -278,6 +278,11 @@ def test_accept_stochastic_validation(L):
     assert _stoch(L, n_max=65) == SHAPE
     assert _stoch(L, V=0) == SHAPE
     assert _stoch(L, V=-5) == SHAPE
+    # no slices for bad shapes; without a device the query finds no compute units and
+    # asks for no workspace (one workgroup per sequence)
+    for B, n_max, V in ((0, 64, 1000), (2, 65, 1000), (2, 0, 1000), (2, 64, 0)):
+        assert L.tree_accept_stochastic_workspace_size(B, n_max, V) == 0
+    assert L.tree_accept_stochastic_workspace_size(4, 64, 128256) == 0
 
 
 def test_budget_thresholds(L):

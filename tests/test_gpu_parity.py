@@ -600,20 +600,29 @@ def _stochastic_case(seed, B, V, n_max=64, scale=2.0, one_hot=False):
     return parent, nn, tok, tgt, p, q, ua, ub
 
 
-def _run_stochastic(parent, nn, tok, p, q, ua, ub):
+def _run_stochastic(parent, nn, tok, p, q, ua, ub, split=True):
     par_d, nn_d = dev_i32(parent), dev_i32(nn)
     anc, _, _, _ = tv.tree_build(par_d, nn_d)
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
-    out = tv.tree_accept_stochastic(par_d, anc, nn_d, dev_i32(tok), f(p), f(q), f(ua), f(ub))
+    out = tv.tree_accept_stochastic(par_d, anc, nn_d, dev_i32(tok), f(p), f(q), f(ua), f(ub),
+                                    split=split)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in out]
 
 
-@pytest.mark.parametrize("seed,B,V", [(1, 6, 1000), (2, 4, 5000), (3, 2, 32000), (4, 8, 37)])
-def test_accept_stochastic_matches_oracle(seed, B, V):
+# split: the vocabulary over several workgroups per sequence where the workspace query
+# asks for one (every case here but the two smallest vocabularies); False: one
+# workgroup per sequence
+SPLIT = [pytest.param(True, id="split"), pytest.param(False, id="onewg")]
+
+
+@pytest.mark.parametrize("split", SPLIT)
+@pytest.mark.parametrize("seed,B,V", [(1, 6, 1000), (2, 4, 5000), (3, 2, 32000), (4, 8, 37),
+                                      (5, 32, 32000), (6, 1, 32000)])
+def test_accept_stochastic_matches_oracle(seed, B, V, split):
     parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V)
     alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
-    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, split)
     assert not indet.any(), f"{int(indet.sum())} sequences excluded"     # none on these seeds
     ok = ~indet
     assert np.array_equal(alen[ok], alen_r[ok])
@@ -623,7 +632,8 @@ def test_accept_stochastic_matches_oracle(seed, B, V):
     assert alen_r.max() >= 1                                         # some candidates passed
 
 
-def test_accept_stochastic_workload4_vocab():
+@pytest.mark.parametrize("split", SPLIT)
+def test_accept_stochastic_workload4_vocab(split):
     """The 70B-shaped workload's own dynamic trees (four sequences of 64 nodes) over its
     128256-token vocabulary, past the LDS cap, against the oracle bit for bit."""
     w = synth.WORKLOADS[4]
@@ -646,31 +656,33 @@ def test_accept_stochastic_workload4_vocab():
     ua = rng.random((B, n_max)).astype(np.float32)
     ub = rng.random(B).astype(np.float32)
     alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
-    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, split)
     assert not indet.any(), f"{int(indet.sum())} sequences excluded"
     assert np.array_equal(alen, alen_r) and np.array_equal(best, best_r)
     assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
     assert alen_r.max() >= 1
 
 
+@pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("seed,B,V", [(12, 5, 40000), (13, 3, 200003)])
-def test_accept_stochastic_large_vocab(seed, B, V):
-    """Vocabularies past the LDS cap (weights recomputed from p and q every pass),
-    against the oracle bit for bit."""
+def test_accept_stochastic_large_vocab(seed, B, V, split):
+    """Vocabularies past the LDS cap (weights recomputed from p and q every pass, or
+    kept per slice), against the oracle bit for bit."""
     parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V)
     alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
-    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, split)
     assert not indet.any(), f"{int(indet.sum())} sequences excluded"
     assert np.array_equal(alen, alen_r) and np.array_equal(best, best_r)
     assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
 
 
+@pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("V", [300, 50000])
-def test_accept_stochastic_greedy_limit_equals_tree_accept(V):
+def test_accept_stochastic_greedy_limit_equals_tree_accept(V, split):
     """One-hot target rows: the device's stochastic walk equals its greedy acceptance
-    (r in LDS, and recomputed past the LDS cap)."""
+    (r in LDS, recomputed past the LDS cap, or in slices)."""
     parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(9, 6, V, one_hot=True)
-    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, split)
     par_d, nn_d = dev_i32(parent), dev_i32(nn)
     anc, depth, _, _ = tv.tree_build(par_d, nn_d)
     g = [t.cpu().numpy() for t in tv.tree_accept(par_d, depth, anc, nn_d, dev_i32(tok), dev_i32(tgt))]
@@ -679,13 +691,46 @@ def test_accept_stochastic_greedy_limit_equals_tree_accept(V):
     assert g[0].max() >= 2
 
 
-def test_accept_stochastic_invalid_tree():
-    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(10, 3, 64)
+@pytest.mark.parametrize("split", SPLIT)
+@pytest.mark.parametrize("V", [64, 20000])
+def test_accept_stochastic_invalid_tree(V, split):
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(10, 3, V)
     parent[1, 5] = 7                                                 # a forward link: rejected
     nn[2] = 0
-    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, split)
     for b in (1, 2):
         assert alen[b] == -1 and best[b] == -1 and bonus[b] == -1 and np.all(path[b] == -1)
+    assert alen[0] >= 0
+
+
+def test_accept_stochastic_split_plan_and_workspace():
+    """The workspace query asks for slices where the vocabulary and the batch leave
+    room (one 64-bit word triple per sequence, node and slice), none for tiny
+    vocabularies or batches past the compute units; a workspace smaller than the query
+    is refused."""
+    L = tv.lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert L.tree_accept_stochastic_workspace_size(1, 64, 300) == 0
+    assert L.tree_accept_stochastic_workspace_size(cus + 1, 64, 32000) == 0
+    assert L.tree_accept_stochastic_workspace_size(64, 64, 128256) == 0      # 8 slices each
+    need = L.tree_accept_stochastic_workspace_size(4, 64, 128256)
+    P = min(64, cus // 4)
+    assert need == (4 * 64 * P * 24 + 255) // 256 * 256
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(11, 4, 3000)
+    par_d, nn_d = dev_i32(parent), dev_i32(nn)
+    anc, _, _, _ = tv.tree_build(par_d, nn_d)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    need = L.tree_accept_stochastic_workspace_size(4, 64, 3000)
+    assert need > 0
+    ws = torch.empty((need,), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty(4, dtype=torch.int32, device=DEV) for _ in range(3)]
+    args = [4, 64, 3000] + [x.data_ptr() for x in (par_d, anc, nn_d, dev_i32(tok), f(p), f(q), f(ua), f(ub))]
+    args += [o.data_ptr() for o in outs] + [None]
+    st = L.tree_accept_stochastic(*args, ws.data_ptr(), need - 8, None)
+    assert st == 5                                                   # TV_ERR_WORKSPACE
+    st = L.tree_accept_stochastic(*args, ws.data_ptr() + 8, need, None)
+    assert st == 5                                                   # misaligned
+    torch.cuda.synchronize()
 
 
 

@@ -14,7 +14,8 @@ EXPORTS = ("tv_abi_version", "tv_status_string", "tree_build", "tree_expand_work
            "tree_expand_rerank", "tree_draft_continue", "tree_cost_lookup", "tree_budget_thresholds",
            "tree_verify_attn_workspace_size", "tree_verify_attn_plan", "tree_verify_attn",
            "tree_verify_attn_noalloc",
-           "tree_accept", "tree_accept_stochastic", "tree_kv_compact",
+           "tree_accept", "tree_accept_stochastic_workspace_size", "tree_accept_stochastic",
+           "tree_kv_compact",
            "tree_candidate_workspace_size", "tree_candidate_logits")
 
 _P = ctypes.c_void_p
@@ -39,8 +40,9 @@ _SIGNATURES = {
     "tree_verify_attn_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _P, _P, _P]),
     "tree_accept": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "tree_accept_stochastic_workspace_size": (_S, [_I, _I, _I]),
     "tree_accept_stochastic": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                    _P]),
+                                    _P, _S, _P]),
     "tree_kv_compact": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
     "tree_candidate_workspace_size": (_S, [_I, _I, _I]),
     "tree_candidate_logits": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),

@@ -312,9 +312,12 @@ def tree_kv_compact(k_tree, v_tree, path, accept_len, k_dst, v_dst, dst_row):
 
 
 def tree_accept_stochastic(parent, anc, n_nodes, token, p_target, q_draft, u_accept, u_bonus,
-                           want_path=True):
+                           want_path=True, split=True):
     """(accept_len, best_node, bonus_token, path): rejection-sampling acceptance.
-    p_target, q_draft float32 [B][n_max][vocab]; u_accept [B][n_max], u_bonus [B]."""
+    p_target, q_draft float32 [B][n_max][vocab]; u_accept [B][n_max], u_bonus [B].
+    split: pass a workspace, so that each sequence's vocabulary is spread over several
+    workgroups when the library's size query asks for one; False: one workgroup per
+    sequence."""
     _need(parent, "parent", torch.int32, 2)
     B, n_max = parent.shape
     _need(anc, "anc", torch.int64, shape=(B, n_max))
@@ -331,8 +334,10 @@ def tree_accept_stochastic(parent, anc, n_nodes, token, p_target, q_draft, u_acc
     best = torch.empty((B,), dtype=torch.int32, device=dev)
     bonus = torch.empty((B,), dtype=torch.int32, device=dev)
     path = torch.empty((B, n_max), dtype=torch.int32, device=dev) if want_path else None
+    need = lib().tree_accept_stochastic_workspace_size(B, n_max, V) if split else 0
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need > 0 else None
     check("tree_accept_stochastic", lib().tree_accept_stochastic(
         B, n_max, V, _ptr(parent), _ptr(anc), _ptr(n_nodes), _ptr(token), _ptr(p_target),
         _ptr(q_draft), _ptr(u_accept), _ptr(u_bonus), _ptr(alen), _ptr(best), _ptr(bonus),
-        _ptr(path), _stream()))
+        _ptr(path), _ptr(ws), need, _stream()))
     return alen, best, bonus, path
