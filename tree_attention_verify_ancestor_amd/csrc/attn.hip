@@ -365,12 +365,16 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
     const int dma_row = lane / (ROWB / 16);
     auto stage_kbase = [&](int st) { return (has_tree && st == 0) ? 0 : c0 + (st - has_tree) * KT; };
     // LDS byte offsets of stage st's K tile and of its V tile from the K tile: the tree
-    // stage has its own area when it fits, the prefix stages cycle through the ring
+    // stage has its own area when it fits, the prefix stages cycle through the ring,
+    // whose K tiles fill its first half and V tiles its second.  The first prefix stage
+    // takes slot 0 (a tree stage in the ring the last slot), so that a loop over the
+    // prefix stages knows each stage's slot at compile time when unrolled by NBUF.
     const int extra = SEP_TREE && has_tree ? 1 : 0;       // stages outside the ring
+    const int rot = has_tree ? 1 : 0;
     auto k_tile = [&](int st) {
-      return (SEP_TREE && has_tree && st == 0) ? RING : ((st - extra) % NBUF) * STAGEB;
+      return (SEP_TREE && has_tree && st == 0) ? RING : ((st - rot + NBUF) % NBUF) * TILEB;
     };
-    auto v_tile = [&](int st) { return (SEP_TREE && has_tree && st == 0) ? TREE_TILEB : TILEB; };
+    auto v_tile = [&](int st) { return (SEP_TREE && has_tree && st == 0) ? TREE_TILEB : NBUF * TILEB; };
     // per-lane byte offset of this thread's first DMA within a full prefix stage (the
     // stage's first key row is added to the uniform base).  DMA i reads ROWS_PER_KB * i
     // rows further on (a uniform term) at a chunk whose index differs by XOR with i & 3
@@ -728,6 +732,46 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
           const s16x4 both[2] = {lo, hi};
           vr.v[ks][dt] = *(const bf16x8*)both;
         };
+        // This lane's LDS addresses in ring slot 0, subtile 0: K operand slice i, and the
+        // V^T operands dt (rows 0-7, rows 8-15 of a 16-key step).  Slot, subtile and step
+        // add multiples of the row size, which leave the XORed chunk bits alone, so any
+        // read in the ring is one of these plus a constant: with the slot known at compile
+        // time the constant is the read's immediate offset (below 64 KB: slots of K in the
+        // ring's first half, of V in its second) and the read needs no address arithmetic.
+        uint32_t kof[DS], vof[DT][2];
+        {
+          const uint32_t ring = lds_addr(smem);
+#pragma unroll
+          for (int i = 0; i < DS; ++i) kof[i] = (ring + koff0) ^ (i << 5);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            vof[dt][0] = (ring + NBUF * TILEB + voff0) ^ (dt << 6);
+            vof[dt][1] = (vof[dt][0] ^ VHI) + 8 * ROWB;
+          }
+        }
+        // the reads of one subtile: at run-time addresses (RtAddr: its K and V^T bases)
+        // or at a compile-time offset from slot 0 (ic<offset>)
+        struct RtAddr {
+          uint32_t k, v;
+        };
+        auto rt = [&](int st, int sub) { return RtAddr{k_addr(st, sub), v_addr(st, sub)}; };
+        auto kread = [&](auto at, int i) __attribute__((always_inline)) {
+          if constexpr (std::is_same_v<decltype(at), RtAddr>) return read_k_slice(at.k, i);
+          else return *(lds_bf16x8*)(uintptr_t)(kof[i] + (uint32_t)decltype(at)::value);
+        };
+        auto vread = [&](auto at, int ks, int dt) __attribute__((always_inline)) {
+          if constexpr (std::is_same_v<decltype(at), RtAddr>) {
+            read_v_op(at.v, ks, dt);
+          } else {
+            constexpr uint32_t O = decltype(at)::value;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(uintptr_t)(vof[dt][0] + O + ks * 16 * ROWB));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(uintptr_t)(vof[dt][1] + O + ks * 16 * ROWB));
+            const s16x4 both[2] = {lo, hi};
+            vr.v[ks][dt] = *(const bf16x8*)both;
+          }
+        };
         // One subtile s, in two phases whose issue order is pinned by scheduling fences.
         // A wave's LDS reads hold up its vector instructions, so the softmax goes beside
         // products with as few reads as possible:
@@ -738,9 +782,10 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         //  2. O^T += V^T P^T of s, each product followed by the reload of its V^T operand
         //     with subtile s+1's, and the last two by the first two K slices of s+2
         //     (st2, sub2).
-        // Where s+1 or s+2 does not exist, valid LDS data is read and the result dropped.
-        auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, int st1,
-                        int sub1, int st2, int sub2) __attribute__((always_inline)) {
+        // Where s+1 or s+2 does not exist, LDS data of the ring is read and the result
+        // dropped.  a1: the reads of s+1, a2: those of s+2.
+        auto step = [&](auto masked_tag, f32x16& s_cur, f32x16& s_nxt, int st, int sub, auto a1,
+                        auto a2) __attribute__((always_inline)) {
           constexpr bool MASKED = decltype(masked_tag)::value;
           constexpr int EPG = 16 / DS;             // weights per product of the next subtile
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -750,9 +795,6 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
             apply_mask(s_cur, stage_kbase(st) + sub * 32 + 4 * g, tree ? n : c1,
                        tree ? qanc[0] : ~0ull);
           }
-          const uint32_t ka1 = k_addr(st1, sub1);
-          const uint32_t va1 = v_addr(st1, sub1);
-          const uint32_t ka2 = k_addr(st2, sub2);
           f32x16 sn = f32x16{};
           float e[16];
           bf16x2 pk[8];
@@ -765,7 +807,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < DS; ++i) {
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % 3], qop[0][i], sn, 0, 0, 0);
-            if (i + 2 < DS) kb[(i + 2) % 3] = read_k_slice(ka1, i + 2);
+            if (i + 2 < DS) kb[(i + 2) % 3] = kread(a1, i + 2);
 #pragma unroll
             for (int j = i * EPG; j < (i + 1) * EPG; ++j) {
               float sv = s_cur[j];
@@ -803,9 +845,9 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
               o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr.v[ks][dt], pb[ks], o[0][dt], 0, 0, 0);
-              read_v_op(va1, ks, dt);
+              vread(a1, ks, dt);
               const int q = ks * DT + dt;
-              if (q >= 2 * DT - 2) kb[q - (2 * DT - 2)] = read_k_slice(ka2, q - (2 * DT - 2));
+              if (q >= 2 * DT - 2) kb[q - (2 * DT - 2)] = kread(a2, q - (2 * DT - 2));
               __builtin_amdgcn_sched_barrier(0);
             }
           s_nxt = sn;
@@ -842,11 +884,11 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
           const bool two1 = more && nsub(1) >= 2;          // stage 1 holds a second subtile
           if (nsub(0) == 2) {
             prefetch_k(0, 1);
-            step(unmasked, sa, sb, 0, 0, 0, 1, more ? 1 : 0, 0);
-            step(masked, sb, sa, 0, 1, more ? 1 : 0, more ? 0 : 1, two1 ? 1 : 0, 1);
+            step(unmasked, sa, sb, 0, 0, rt(0, 1), rt(more ? 1 : 0, 0));
+            step(masked, sb, sa, 0, 1, rt(more ? 1 : 0, more ? 0 : 1), rt(two1 ? 1 : 0, 1));
           } else {
             prefetch_k(more ? 1 : 0, 0);
-            step(unmasked, sa, sb, 0, 0, more ? 1 : 0, 0, two1 ? 1 : 0, two1 ? 1 : 0);
+            step(unmasked, sa, sb, 0, 0, rt(more ? 1 : 0, 0), rt(two1 ? 1 : 0, two1 ? 1 : 0));
             sa = sb;
           }
           x = 1;
@@ -857,20 +899,36 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         // that the steps can read its K and V^T while their products run; one code path
         // (where there is no next stage the reads repeat this stage's)
         const int full_end = has_tree + n_full;
+        // unrolled over the ring: stage x in slot S, the next stage in slot S+1 (read
+        // even where it does not exist; those results are dropped)
+        auto ring_stage = [&](auto slot_tag, int xx) __attribute__((always_inline)) {
+          constexpr int S = decltype(slot_tag)::value;
+          constexpr int S1 = (S + 1) % NBUF;
+          if (xx >= 1 && xx + 1 < nst) open_stage(xx + 1);
+          step(unmasked, sa, sb, xx, 0, ic<S * TILEB + 32 * ROWB>{}, ic<S1 * TILEB>{});
+          step(unmasked, sb, sa, xx, 1, ic<S1 * TILEB>{}, ic<S1 * TILEB + 32 * ROWB>{});
+        };
+        static_assert(NBUF == 4 && NSW == 2, "the unrolled loop takes four slots of two subtiles");
+        for (; x + 3 < full_end; x += 4) {           // stage x is in slot 0 here
+          ring_stage(ic<0>{}, x);
+          ring_stage(ic<1>{}, x + 1);
+          ring_stage(ic<2>{}, x + 2);
+          ring_stage(ic<3>{}, x + 3);
+        }
         for (; x < full_end; ++x) {
           const bool more = x + 1 < nst;
           const bool two = more && nsub(x + 1) >= 2;
           if (x >= 1 && more) open_stage(x + 1);
-          step(unmasked, sa, sb, x, 0, x, 1, more ? x + 1 : x, 0);
-          step(unmasked, sb, sa, x, 1, more ? x + 1 : x, more ? 0 : 1, two ? x + 1 : x, 1);
+          step(unmasked, sa, sb, x, 0, rt(x, 1), rt(more ? x + 1 : x, 0));
+          step(unmasked, sb, sa, x, 1, rt(more ? x + 1 : x, more ? 0 : 1), rt(two ? x + 1 : x, 1));
         }
         // a partial last prefix stage (masked; opened by the loop or above)
         if (x < nst) {
           if (nsub(x) >= 2) {
-            step(masked, sa, sb, x, 0, x, 1, x, 0);
-            step(masked, sb, sa, x, 1, x, 1, x, 1);
+            step(masked, sa, sb, x, 0, rt(x, 1), rt(x, 0));
+            step(masked, sb, sa, x, 1, rt(x, 1), rt(x, 1));
           } else {
-            step(masked, sa, sb, x, 0, x, 0, x, 0);
+            step(masked, sa, sb, x, 0, rt(x, 0), rt(x, 0));
           }
         }
         // weights past the fixed reference's range show in the row sum (all terms are
