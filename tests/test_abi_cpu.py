@@ -173,13 +173,10 @@ def test_attn_workspace_size(L):
 def test_attn_plan(L):
     """The launch-plan query: host only; each row-count regime takes its shape (a 70B-shaped
     batch with 512 rows per KV head: eight waves of one 32-row tile, 256 rows a
-    workgroup, four chunks of 8192 keys: one workgroup per CU; a batch of eight or more
-    sequences about two per CU)."""
+    workgroup, eight chunks of 4096 keys)."""
     plan = (ctypes.c_int32 * 8)()
     assert L.tree_verify_attn_plan(1, 4, 64, 64, 8, 128, 32768, plan) == OK
-    assert list(plan) == [8, 8, 1, 1, 256, 8192, 4, 256]
-    assert L.tree_verify_attn_plan(1, 32, 64, 32, 8, 128, 8192, plan) == OK
-    assert list(plan) == [8, 8, 1, 1, 256, 4096, 2, 512]
+    assert list(plan) == [8, 8, 1, 1, 256, 4096, 8, 512]
     assert L.tree_verify_attn_plan(1, 2, 32, 2, 2, 128, 3000, plan) == OK
     assert list(plan)[:5] == [4, 1, 4, 1, 32]
     assert L.tree_verify_attn_plan(1, 2, 64, 4, 2, 128, 3000, plan) == OK

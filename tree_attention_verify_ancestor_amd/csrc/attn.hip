@@ -110,12 +110,9 @@ static AttnPlan make_plan(int B, int n_max, int Hq, int Hkv, int D, int max_pref
   p.n_rb = (R + p.rows_per_wg - 1) / p.rows_per_wg;
   const int kt = stage_keys(p.wk);
   p.units = B * Hkv * p.n_rb;
-  // Every shape holds 128-160 KB of LDS, one workgroup per CU.  A batch of few
-  // sequences (equal-length ones, as a rule) takes one workgroup per CU over 256 CUs:
-  // a second round of equal workgroups only adds a gap between the rounds and twice the
-  // partials.  A larger, ragged batch takes about two per CU, so that the short items
-  // fill in behind the long ones.  Every chunk at least two stages.
-  const long target = (split_rows || B < kRankMinBatch) ? 256 : 512;
+  // about two workgroups per CU over 256 CUs (one for split rows); every chunk at
+  // least two stages
+  const long target = split_rows ? 256 : 512;
   long want = (target + p.units - 1) / p.units;
   if (want < 1) want = 1;
   long ck = (max_prefix + want - 1) / want;
