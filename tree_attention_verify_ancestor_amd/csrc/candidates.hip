@@ -111,8 +111,10 @@ __global__ __launch_bounds__(256) void cand_z_kernel(int rows, int d, int r, con
 // Besides the scores, each wave records, per row, the largest key (cand_key) of its
 // 8 * TPT tokens (a score group) in gmax[row][group], group = the wave's index in the
 // grid; tokens past the vocabulary count as key 0.
-template <int ROWS, int TPT, int RMAX>
-__global__ __launch_bounds__(kScoreWaves * kWave) void cand_score_kernel(
+// WPE: waves per SIMD the register allocation must leave room for (8 rows fit three
+// waves in 168 registers without spills; 10 rows would spill)
+template <int ROWS, int TPT, int RMAX, int WPE>
+__global__ __launch_bounds__(kScoreWaves * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void cand_score_kernel(
     int rows, int r, int V, const __bf16* __restrict__ Bm, const double* __restrict__ z64,
     float* __restrict__ logits, uint32_t* __restrict__ gmax, int ng) {
   static_assert(ROWS % 2 == 0 && ROWS <= kCandGroup, "rows in pairs, at most one group");
@@ -624,7 +626,7 @@ static void launch_score_rows(int rows, int r, int vocab, const __bf16* Bm, cons
   constexpr int TPT = ROWS <= 12 ? 4 : 2;             // tokens per lane: acc stays <= 48 doubles
   const int per_wg = kScoreWaves * 8 * TPT;
   const dim3 grid((vocab + per_wg - 1) / per_wg, (rows + kCandGroup - 1) / kCandGroup);
-  hipLaunchKernelGGL((cand_score_kernel<ROWS, TPT, RMAX>), grid, dim3(kScoreWaves * kWave), 0, stream,
+  hipLaunchKernelGGL((cand_score_kernel<ROWS, TPT, RMAX, ROWS <= 8 ? 3 : 1>), grid, dim3(kScoreWaves * kWave), 0, stream,
                      rows, r, vocab, Bm, z64, logits, gmax, ng);
 }
 template <int RMAX>
