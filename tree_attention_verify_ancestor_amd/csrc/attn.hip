@@ -181,6 +181,16 @@ using ic = std::integral_constant<int, N>;
 
 enum StageMode { kFull = 0, kMasked = 1 };
 
+// Key chunks per workgroup for a sequence with R rows per KV head.  The plan is sized by
+// n_max: where a tree fills every row block of the eight-wave shape (256 rows a block),
+// a workgroup takes two adjacent chunks as one pass, so that such a call runs as many
+// workgroups as one with half the rows (about one per CU) instead of a second round;
+// smaller trees leave the row blocks past their rows idle and keep one chunk each.  The
+// attention kernel, its ranking of pairs and the merge all take the span from here.
+__device__ __forceinline__ int chunk_span(const AttnArgs& a, int R) {
+  return a.rows_per_wg == 256 && a.n_rb >= 2 && R > (a.n_rb - 1) * a.rows_per_wg ? 2 : 1;
+}
+
 template <int D, int WQ, int WK, int QT>
 __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   constexpr int W = WQ * WK;
@@ -249,9 +259,10 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       if (nj != n0 || Lj != L0) *s_ragged = 1;
       int w = 0;
       if (nj >= 1 && nj <= a.n_max && Lj >= 0 && Lj <= a.max_prefix) {
+        const int sj = chunk_span(a, nj * a.G);
         const int64_t lo = (int64_t)cj * a.chunk_keys;
-        const int keys = (int)max((int64_t)0, min((int64_t)a.chunk_keys, Lj - lo)) + (cj == 0 ? nj : 0);
-        w = (cj == 0 || lo < Lj) ? keys * ((nj * a.G + 31) / 32) : 0;
+        const int keys = (int)max((int64_t)0, min((int64_t)sj * a.chunk_keys, Lj - lo)) + (cj == 0 ? nj : 0);
+        w = cj % sj == 0 && (cj == 0 || lo < Lj) ? keys * ((nj * a.G + 31) / 32) : 0;
       }
       s_work[j] = w;
     }
@@ -311,9 +322,10 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
   const int G = a.G;
   const int R = n_ok ? n * G : 0;
   const int row0 = rb * a.rows_per_wg;
+  const int span = chunk_span(a, R);
   const int c0 = chunk * a.chunk_keys;
-  const int c1 = min(L, c0 + a.chunk_keys);
-  const bool active = seq_ok && row0 < R && (chunk == 0 || c0 < L);
+  const int c1 = min(L, c0 + span * a.chunk_keys);
+  const bool active = seq_ok && row0 < R && chunk % span == 0 && (chunk == 0 || c0 < L);
 
   if (active) {
     const int has_tree = chunk == 0 ? 1 : 0;
@@ -1042,7 +1054,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       }
     }
     __syncthreads();
-    const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
+    const int nc = L > 0 ? (L + span * a.chunk_keys - 1) / (span * a.chunk_keys) : 1;
     constexpr int D4 = D / 4;
     // only the rows that hold tree nodes (chunk 0 zero-fills the others); unrolled, so
     // that the LDS reads of several rows are in flight together
@@ -1131,7 +1143,8 @@ __global__ __launch_bounds__(kCombineLanes * CR) void attn_combine(AttnArgs a) {
   const int64_t Lw = a.offsets[b + 1] - a.offsets[b];
   if (n < 1 || n > a.n_max || a.offsets[b] < 0 || Lw < 0 || Lw > a.max_prefix || i >= n) return;
   const int L = (int)Lw;
-  const int nc = L > 0 ? (L + a.chunk_keys - 1) / a.chunk_keys : 1;
+  const int span = chunk_span(a, n * a.G);
+  const int nc = L > 0 ? (L + span * a.chunk_keys - 1) / (span * a.chunk_keys) : 1;
   if (nc <= 1) return;
   const int G = a.G;
   const int kvh = h / G;
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__(kCombineLanes * CR) void attn_combine(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < kCombineBatch; ++j) {
       if (c0 + j < nc) {
-        const size_t slot = slot0 + (size_t)(c0 + j) * a.rows_per_wg;
+        const size_t slot = slot0 + (size_t)(c0 + j) * span * a.rows_per_wg;
         ml[j] = a.part_ml[slot];
 #pragma unroll
         for (int v = 0; v < V4; ++v) po[j][v] = *(const f32x4*)(a.part_o + slot * D + d0 + 4 * v);
