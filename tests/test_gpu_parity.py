@@ -212,6 +212,10 @@ SMALL_ATTN = [  # (B, Hq, Hkv, D, prefix lengths, node counts)
     (12, 16, 4, 64, (100, 2000, 50, 700, 1, 0, 3000, 256, 128, 900, 1500, 30),
      (5, 64, 30, 12, 64, 2, 40, 64, 7, 19, 64, 26)),
     (8, 4, 4, 64, (500,) * 8, (20,) * 8),
+    # 1024 rows per KV head, four 256-row blocks: trees filling all four take two key
+    # chunks per workgroup, the others one
+    (4, 32, 2, 128, (3000, 2100, 777, 0), (64, 40, 1, 61)),
+    (4, 32, 2, 64, (1500, 3000, 0, 2500), (61, 64, 50, 64)),
 ]
 
 
@@ -253,6 +257,7 @@ ATTN_SHAPES = {
     "256 rows in few units: 64-row units": (2, 64, 4, 2, (4, 1, 4, 2)),
     "128 rows: four row groups x two key halves": (2, 64, 2, 2, (8, 4, 2, 1)),
     "512 rows: eight waves of one tile": (4, 64, 8, 8, (8, 8, 1, 1)),
+    "1024 rows: four row blocks of eight waves": (4, 64, 16, 2, (8, 8, 1, 1)),
 }
 # the same shapes with nine ragged sequences (ranked by work where eight waves own one
 # tile each: the ranking applies from eight sequences on)
