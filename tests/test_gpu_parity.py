@@ -681,6 +681,24 @@ def test_accept_stochastic_large_vocab(seed, B, V, split):
     assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
 
 
+@pytest.mark.parametrize("seed,B,V,n_max", [(21, 128, 16385, 16), (22, 200, 40000, 8)])
+def test_accept_stochastic_split_plan_edges(seed, B, V, n_max):
+    """The sliced path at its plan's edges: 128 sequences of 16385 tokens take the
+    fewest slices it uses (two of 8193 tokens: 256 compute units over 128 sequences,
+    16384 tokens of LDS per slice); 200 sequences of 40000 tokens are past the compute
+    units and stream with one workgroup each.  Against the oracle bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    need = tv.lib().tree_accept_stochastic_workspace_size(B, n_max, V)
+    if cus >= 256:
+        assert (need > 0) == (B == 128), need
+    parent, nn, tok, tgt, p, q, ua, ub = _stochastic_case(seed, B, V, n_max=n_max)
+    alen_r, best_r, bonus_r, path_r, indet = oracle.tree_accept_stochastic(parent, tok, nn, p, q, ua, ub)
+    alen, best, bonus, path = _run_stochastic(parent, nn, tok, p, q, ua, ub, True)
+    assert not indet.any(), f"{int(indet.sum())} sequences excluded"
+    assert np.array_equal(alen, alen_r) and np.array_equal(best, best_r)
+    assert np.array_equal(bonus, bonus_r) and np.array_equal(path, path_r)
+
+
 @pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("V", [300, 50000])
 def test_accept_stochastic_greedy_limit_equals_tree_accept(V, split):
