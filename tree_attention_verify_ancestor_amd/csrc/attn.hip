@@ -1027,6 +1027,47 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         }
       });
     }
+    const int nc = L > 0 ? (L + span * a.chunk_keys - 1) / (span * a.chunk_keys) : 1;
+    if constexpr (WK == 1 && QT == 1) {
+      // ---- one 32-row tile per wave and no key split: each wave writes its rows
+      // straight from its accumulators (the two lanes of a row store 32 contiguous
+      // bytes per instruction), with no LDS staging and no barrier: the final rows when
+      // the sequence's prefix fits in one chunk, else unnormalised partials for
+      // attn_combine.  The same arithmetic as the staged path below.
+      const float lt = sum_halves(l_run[0]);
+      const int i = wave * 32 + ql;                    // row within the workgroup
+      const int rho_i = row0 + i;
+      if (wave_live && rho_i < R) {
+        const float M = m_run[0];
+        const float sc = __builtin_amdgcn_exp2f(M - (M == -INFINITY ? 0.f : M));   // 0 without keys
+        const float lsum = lt * sc;
+        if (nc == 1) {
+          const int node = rho_i / G;
+          const int head = kvh * G + rho_i % G;
+          const size_t orow = ((size_t)b * a.n_max + node) * a.Hq + head;
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              __bf16 ob4[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ob4[e] = (__bf16)(o[0][dt][4 * r4 + e] * sc * inv);
+              *(s16x4*)(a.out + orow * D + 32 * dt + 8 * r4 + 4 * g) = *(const s16x4*)ob4;
+            }
+          if (a.lse && g == 0) a.lse[orow] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : 0.f;
+        } else {
+          const size_t slot = ((size_t)unit * a.n_chunks + chunk) * a.rows_per_wg + i;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              *(f32x4*)(a.part_o + slot * D + 32 * dt + 8 * r4 + 4 * g) =
+                  f32x4{o[0][dt][4 * r4], o[0][dt][4 * r4 + 1], o[0][dt][4 * r4 + 2], o[0][dt][4 * r4 + 3]} * sc;
+          if (g == 0) a.part_ml[slot] = make_float2(M, lsum);
+        }
+      }
+    } else {
     // ---- every wave parks its rows (unnormalised O, reference m, sum l) in LDS, then
     // the whole workgroup combines the key-split waves of each row and writes the
     // chunk's output with coalesced stores: the final rows when the sequence's prefix
@@ -1054,7 +1095,6 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
       }
     }
     __syncthreads();
-    const int nc = L > 0 ? (L + span * a.chunk_keys - 1) / (span * a.chunk_keys) : 1;
     constexpr int D4 = D / 4;
     // only the rows that hold tree nodes (chunk 0 zero-fills the others); unrolled, so
     // that the LDS reads of several rows are in flight together
@@ -1097,6 +1137,7 @@ __global__ __launch_bounds__(64 * WQ * WK) void attn_bf16(AttnArgs a) {
         *(f32x4*)(a.part_o + slot * D + d) = acc;
         if (d == 0) a.part_ml[slot] = make_float2(M, lsum);
       }
+    }
     }
   }
 
